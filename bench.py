@@ -1,0 +1,249 @@
+"""Benchmark of the MoE FFN layer hot path on one MI355X.
+
+One step = one forward + backward pass of the whole layer (routing, permute,
+grouped SwiGLU GEMMs, combine, and their backward) over T=8192 tokens at
+dots.llm1 shapes (H=5120, 128 routed experts of width 1408, top-6, 2 shared
+experts), synthetic seeded inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "prefill", "skew", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens of the same batch the CPU oracle runs on")
+    return ap.parse_args()
+
+
+class Layer:
+    """All buffers of one fwd+bwd step, allocated once; step() only launches."""
+
+    def __init__(self, M, g, K):
+        import torch
+        self.M, self.g, self.K = M, g, K
+        x = g["x"]
+        T, H = x.shape
+        E, twoF, _ = g["w1"].shape
+        F = twoF // 2
+        dev = x.device
+        bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+        self.T, self.H, self.E, self.F = T, H, E, F
+        self.w1f, self.w2f = M.fuse_shared(g["w1_sh"], g["w2_sh"])
+        SF = self.w2f.shape[2]
+        m_cap = M.moe_capacity_rows(T, E, K)
+        A = M.moe_align()
+        e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=dev)
+        self.b = dict(
+            topk_idx=e(T, K, dt=i32), topk_w=e(T, K, dt=f32), topk_s=e(T, K, dt=f32),
+            perm=dict(counts=e(E, dt=i32), offsets=e(E + 1, dt=i32), row_of=e(T, K, dt=i32),
+                      src_token=e(m_cap, dt=i32), tile_expert=e(m_cap // A, dt=i32),
+                      x_rows=e(m_cap, H)),
+            perm_ws=e(max(M.moe_permute_workspace_bytes(T, E, K), 1), dt=torch.uint8),
+            act=e(m_cap, 2 * F), h=e(m_cap, F), y_rows=e(m_cap, H),
+            act_sh=e(T, 2 * SF), h_sh=e(T, SF), y_sh=e(T, H), y=e(T, H),
+            dy_rows=e(m_cap, H), dg=e(T, K, dt=f32), dact=e(m_cap, 2 * F), dx_rows=e(m_cap, H),
+            dw1=e(E, 2 * F, H), dw2=e(E, H, F),
+            dact_sh=e(T, 2 * SF), dx_sh=e(T, H), dw1_sh=e(1, 2 * SF, H), dw2_sh=e(1, H, SF),
+            dw_router=e(H, E, dt=f32), dx_router=e(T, H, dt=f32),
+            rb_ws=e(M.moe_route_bwd_workspace_bytes(T, H, E, K), dt=torch.uint8),
+            dx=e(T, H))
+        self.ev = None
+
+    def forward(self, ev=None):
+        M, g, b, K = self.M, self.g, self.b, self.K
+        p = b["perm"]
+        M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"])
+        M.moe_permute(b["topk_idx"], g["x"], self.E, out=p, ws=b["perm_ws"])
+        if ev is not None:
+            ev[0].record()
+        M.moe_grouped_gate_up_fwd(p["x_rows"], g["w1"], p["offsets"], p["counts"], p["tile_expert"],
+                                  act=b["act"], h=b["h"])
+        if ev is not None:
+            ev[1].record()
+        M.moe_grouped_down_fwd(b["h"], g["w2"], p["offsets"], p["counts"], p["tile_expert"],
+                               y_rows=b["y_rows"])
+        M.moe_grouped_swiglu_fwd(g["x"], self.w1f, self.w2f, act=b["act_sh"], h=b["h_sh"],
+                                 y_rows=b["y_sh"])
+        if ev is not None:
+            ev[2].record()
+        M.moe_combine(b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"])
+
+    def backward(self, ev=None):
+        M, g, b = self.M, self.g, self.b
+        p = b["perm"]
+        M.moe_combine_bwd(g["dy"], b["y_rows"], p["row_of"], b["topk_w"], dy_rows=b["dy_rows"], dg=b["dg"])
+        if ev is not None:
+            ev[3].record()
+        M.moe_grouped_swiglu_bwd(p["x_rows"], g["w1"], g["w2"], b["act"], b["h"], b["dy_rows"],
+                                 p["offsets"], p["counts"], p["tile_expert"], dact=b["dact"],
+                                 dx_rows=b["dx_rows"], dw1=b["dw1"], dw2=b["dw2"])
+        M.moe_grouped_swiglu_bwd(g["x"], self.w1f, self.w2f, b["act_sh"], b["h_sh"], g["dy"],
+                                 dact=b["dact_sh"], dx_rows=b["dx_sh"], dw1=b["dw1_sh"],
+                                 dw2=b["dw2_sh"])
+        if ev is not None:
+            ev[4].record()
+        M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
+                        p["offsets"], p["counts"], dw_router=b["dw_router"],
+                        dx_router=b["dx_router"], ws=b["rb_ws"])
+        M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+
+
+class LazyExperts:
+    """Per-expert fp32 view of a host bf16 tensor [E, R, C] for the oracle."""
+
+    def __init__(self, t):
+        self.t = t.detach().to("cpu")
+        self.shape = tuple(self.t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].float().numpy()
+
+
+def cpu_baseline(w, g, n_tokens):
+    """The CPU oracle, untouched, on the first n_tokens tokens of the batch
+    (forward + backward).  Reported in the same unit (useful TFLOP/s)."""
+    import torch
+    from oracle import moe_oracle as O
+    from fine_grained_moe_amd.synthetic import useful_flops
+    tn = lambda t: t.detach().float().cpu().numpy()
+    sub = dict(x=tn(g["x"][:n_tokens]), w_router=tn(g["w_router"]), bias=tn(g["bias"]),
+               w1=LazyExperts(g["w1"]), w2=LazyExperts(g["w2"]),
+               w1_sh=tn(g["w1_sh"]), w2_sh=tn(g["w2_sh"]))
+    dy = tn(g["dy"][:n_tokens]) if "dy" in g else None
+    backward = dy is not None
+    threads = torch.get_num_threads()
+    t0 = time.perf_counter()
+    fwd = O.forward(sub, w.K, 128)
+    if backward:
+        O.backward(sub, fwd, dy)
+    dt = time.perf_counter() - t0
+    flops = useful_flops(w.with_(T=n_tokens), backward)
+    cores = len(os.sched_getaffinity(0))
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
+                        f"first {n_tokens} of the {w.T} tokens at the same shapes, one run, "
+                        f"{dt:.1f} s; BLAS threads {threads}"),
+                seconds=dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the layer's multi-GPU "
+              "sharding (expert parallel all-to-all) is not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from fine_grained_moe_amd import moe as M
+    from fine_grained_moe_amd.synthetic import WORKLOADS, generate_torch, useful_flops, gemm_useful_flops
+
+    w = WORKLOADS[args.workload]
+    backward = args.workload == "fwdbwd"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = generate_torch(w, dev, with_dy=True)
+    layer = Layer(M, g, w.K)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        layer.forward(ev)
+        if backward:
+            layer.backward(ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps; events inside bracket the grouped GEMMs
+    n_ev = 5
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    gate_up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_fwd_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    gemm_bwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if backward else 0.0
+
+    # forward alone, timed the same way
+    torch.cuda.synchronize()
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        layer.forward()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+
+    flops = useful_flops(w, backward)
+    tflops = flops / (ms * 1e-3) / 1e12
+    fwd_tflops = useful_flops(w, False) / (fwd_ms * 1e-3) / 1e12
+    gemm_flops = gemm_useful_flops(w, backward)
+    gemm_ms = gemm_fwd_ms + gemm_bwd_ms
+    # the gate/up GEMM of the routed experts: useful flops T*K*2H*2F per launch
+    gate_up_flops = float(w.T) * w.K * 2 * w.H * 2 * w.F
+    achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+    counts = layer.b["perm"]["counts"].cpu().numpy()
+
+    out = {
+        "metric": "MoE layer useful TFLOP/s at T=8192 (fwd, fwd+bwd); % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"dots.llm1 MoE FFN layer {'forward+backward' if backward else 'forward'}"
+                                f", T={w.T}, H={w.H}, {w.E} routed experts of width {w.F}, top-{w.K}"
+                                f", {w.S} shared experts"),
+                   "T": w.T, "H": w.H, "E": w.E, "F": w.F, "K": w.K, "S": w.S, "seed": w.seed},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_pct_of_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "gemm_ms": round(gemm_ms, 4),
+        "routed_nonempty_experts": int((counts > 0).sum()),
+        "roofline": {"kernel": "grouped_gemm gate/up + SwiGLU (routed experts)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "launch_ms": round(gate_up_ms, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,257 @@
+// C ABI of the MoE layer library: host-side argument checks, then launches.
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing and touches no device state.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+moe_status_t fail(moe_status_t st, const char* fn, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", fn, what);
+  return st;
+}
+
+moe_status_t hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return MOE_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", fn, hipGetErrorString(e));
+  return MOE_ERR_HIP;
+}
+
+#define REQUIRE(cond, st, msg) \
+  do {                         \
+    if (!(cond)) return fail(st, __func__, msg); \
+  } while (0)
+
+moe_status_t check_dims(const char* fn, int32_t T, int32_t H, int32_t E, int32_t K) {
+  if (T < 0 || H <= 0 || E <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "T<0 or H,E,K<=0");
+  if (K > E) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "K > E");
+  if (E > 128 || K > 16) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "E > 128 or K > 16");
+  if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H % 64 != 0");
+  if ((int64_t)T * K >= (int64_t)1 << 30) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "T*K too large");
+  return MOE_OK;
+}
+
+int64_t capacity(int32_t T, int32_t E, int32_t K) {
+  const int64_t a = moe::kAlign;
+  int64_t n = (int64_t)T * K + (int64_t)E * (a - 1);
+  return (n + a - 1) / a * a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+int32_t moe_align(void) { return moe::kAlign; }
+
+int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K) {
+  if (T < 0 || E <= 0 || K <= 0) return -1;
+  return capacity(T, E, K);
+}
+
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
+  (void)K;
+  if (T < 0 || E <= 0) return 0;
+  return moe::permute_workspace_bytes(T, E);
+}
+
+size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K) {
+  if (T < 0 || H <= 0 || E <= 0 || K <= 0) return 0;
+  return moe::route_bwd_workspace_bytes(capacity(T, E, K), H, E);
+}
+
+moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
+                       const float* w_router, const float* bias, int32_t* topk_idx,
+                       float* topk_w, float* topk_s, void* stream) {
+  moe_status_t st = check_dims(__func__, T, H, E, K);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && w_router && bias && topk_idx && topk_w, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_route(T, H, E, K, x, w_router, bias, topk_idx, topk_w, topk_s,
+                                      (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t align,
+                         const int32_t* topk_idx, const uint16_t* x, int64_t m_cap,
+                         int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                         int32_t* tile_expert, uint16_t* x_rows, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status_t st = check_dims(__func__, T, H, E, K);
+  if (st) return st;
+  REQUIRE(align == moe::kAlign, MOE_ERR_UNSUPPORTED_SHAPE, "align != moe_align()");
+  REQUIRE(m_cap >= capacity(T, E, K) && m_cap % align == 0 && m_cap < ((int64_t)1 << 31),
+          MOE_ERR_INVALID_ARGUMENT, "m_cap below moe_capacity_rows or not a multiple of align");
+  REQUIRE(counts && offsets && src_token && tile_expert, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(T == 0 || (topk_idx && x && row_of && x_rows), MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), MOE_ERR_WORKSPACE_TOO_SMALL,
+          "workspace too small");
+  return hip_status(moe::launch_permute(T, H, E, K, align, topk_idx, x, m_cap, counts, offsets,
+                                        row_of, src_token, tile_expert, x_rows, ws,
+                                        (hipStream_t)stream),
+                    __func__);
+}
+
+static moe_status_t check_grouped(const char* fn, int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                  const int32_t* offsets, const int32_t* counts,
+                                  const int32_t* tile_expert) {
+  if (G <= 0 || m_rows < 0 || H <= 0 || F <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "G,H,F<=0 or m_rows<0");
+  if (H % 64 != 0 || F % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H % 64 or F % 32 != 0");
+  if (m_rows >= ((int64_t)1 << 31)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "m_rows too large");
+  const bool dense = offsets == nullptr && counts == nullptr && tile_expert == nullptr;
+  const bool grouped = offsets != nullptr && counts != nullptr && tile_expert != nullptr;
+  if (!dense && !grouped)
+    return fail(MOE_ERR_INVALID_ARGUMENT, fn, "offsets/counts/tile_expert must be all set or all NULL");
+  if (dense && G != 1) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "dense call needs G == 1");
+  if (grouped && m_rows % moe::kAlign != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, fn, "grouped m_rows must be a multiple of moe_align()");
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_swiglu_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* x_rows,
+                                    const uint16_t* w1, const uint16_t* w2, uint16_t* act,
+                                    uint16_t* h, uint16_t* y_rows, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(x_rows && w1 && w2 && h && y_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = moe::launch_gemm_gate_up(G, m_rows, H, F, offsets, counts, tile_expert, x_rows,
+                                          w1, act, h, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemm_down(G, m_rows, H, F, offsets, counts, tile_expert, h, w2, y_rows, s);
+  return hip_status(e, __func__);
+}
+
+moe_status_t moe_grouped_gate_up_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                     const int32_t* offsets, const int32_t* counts,
+                                     const int32_t* tile_expert, const uint16_t* x_rows,
+                                     const uint16_t* w1, uint16_t* act, uint16_t* h,
+                                     void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(x_rows && w1 && h, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_gate_up(G, m_rows, H, F, offsets, counts, tile_expert,
+                                             x_rows, w1, act, h, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_grouped_down_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                  const int32_t* offsets, const int32_t* counts,
+                                  const int32_t* tile_expert, const uint16_t* h,
+                                  const uint16_t* w2, uint16_t* y_rows, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(h && w2 && y_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_down(G, m_rows, H, F, offsets, counts, tile_expert, h, w2,
+                                          y_rows, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_combine(int32_t T, int32_t H, int32_t K, const uint16_t* y_rows,
+                         const int32_t* row_of, const float* topk_w, const uint16_t* y_shared,
+                         uint16_t* y, void* stream) {
+  REQUIRE(T >= 0 && H > 0 && K > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,K<=0");
+  REQUIRE(H % 64 == 0 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "H % 64 != 0 or K > 16");
+  if (T == 0) return MOE_OK;
+  REQUIRE(y_rows && row_of && topk_w && y, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_combine(T, H, K, y_rows, row_of, topk_w, y_shared, y,
+                                        (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_combine_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dy,
+                             const uint16_t* y_rows, const int32_t* row_of, const float* topk_w,
+                             uint16_t* dy_rows, float* dg, void* stream) {
+  REQUIRE(T >= 0 && H > 0 && K > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,K<=0");
+  REQUIRE(H % 64 == 0 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "H % 64 != 0 or K > 16");
+  if (T == 0) return MOE_OK;
+  REQUIRE(dy && y_rows && row_of && topk_w && dy_rows && dg, MOE_ERR_INVALID_ARGUMENT,
+          "null pointer");
+  return hip_status(moe::launch_combine_bwd(T, H, K, dy, y_rows, row_of, topk_w, dy_rows, dg,
+                                            (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* x_rows,
+                                    const uint16_t* w1, const uint16_t* w2, const uint16_t* act,
+                                    const uint16_t* h, const uint16_t* dy_rows, uint16_t* dact,
+                                    uint16_t* dx_rows, uint16_t* dw1, uint16_t* dw2,
+                                    void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  REQUIRE(x_rows && w1 && w2 && act && h && dy_rows && dact && dx_rows && dw1 && dw2,
+          MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (m_rows > 0) {
+    e = moe::launch_gemm_dgrad_down(G, m_rows, H, F, offsets, counts, tile_expert, dy_rows, w2,
+                                    act, dact, s);
+    if (e == hipSuccess)
+      e = moe::launch_gemm_dgrad_up(G, m_rows, H, F, offsets, counts, tile_expert, dact, w1,
+                                    dx_rows, s);
+  }
+  // weight gradients are written for every group, also when it has no rows
+  if (e == hipSuccess)
+    e = moe::launch_gemm_wgrad_down(G, m_rows, H, F, offsets, counts, dy_rows, h, dw2, s);
+  if (e == hipSuccess)
+    e = moe::launch_gemm_wgrad_up(G, m_rows, H, F, offsets, counts, dact, x_rows, dw1, s);
+  return hip_status(e, __func__);
+}
+
+moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x_rows,
+                           const float* w_router, const int32_t* topk_idx, const float* topk_s,
+                           const float* dg, const int32_t* row_of, const int32_t* offsets,
+                           const int32_t* counts, float* dw_router, float* dx_router, void* ws,
+                           size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(__func__, T, H, E, K);
+  if (st) return st;
+  REQUIRE(w_router && offsets && counts && dw_router, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(T == 0 || (x_rows && topk_idx && topk_s && dg && row_of && dx_router),
+          MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_workspace_bytes(T, H, E, K),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  // T == 0 still writes the (zero) router weight gradient
+  return hip_status(moe::launch_route_bwd(T, H, E, K, x_rows, w_router, topk_idx, topk_s, dg,
+                                          row_of, offsets, counts, dw_router, dx_router, ws,
+                                          (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx_rows,
+                             const int32_t* row_of, const uint16_t* dx_shared,
+                             const float* dx_router, uint16_t* dx, void* stream) {
+  REQUIRE(T >= 0 && H > 0 && K > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,K<=0");
+  REQUIRE(H % 64 == 0 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "H % 64 != 0 or K > 16");
+  if (T == 0) return MOE_OK;
+  REQUIRE(dx_rows && row_of && dx, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_unpermute_add(T, H, K, dx_rows, row_of, dx_shared, dx_router, dx,
+                                              (hipStream_t)stream),
+                    __func__);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal launchers of the MoE kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kAlign = 128;  // grouped-GEMM row tile = segment alignment
+
+hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
+                        const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
+                        hipStream_t s);
+
+size_t permute_workspace_bytes(int T, int E);
+hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
+                          const uint16_t* x, int64_t m_cap, int32_t* counts, int32_t* offsets,
+                          int32_t* row_of, int32_t* src_token, int32_t* tile_expert,
+                          uint16_t* x_rows, void* ws, hipStream_t s);
+
+hipError_t launch_gemm_gate_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                               const int32_t* counts, const int32_t* tile_expert,
+                               const uint16_t* x_rows, const uint16_t* w1, uint16_t* act,
+                               uint16_t* h, hipStream_t s);
+hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                            const int32_t* counts, const int32_t* tile_expert,
+                            const uint16_t* h, const uint16_t* w2, uint16_t* y_rows,
+                            hipStream_t s);
+hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                                  const int32_t* counts, const int32_t* tile_expert,
+                                  const uint16_t* dy_rows, const uint16_t* w2,
+                                  const uint16_t* act, uint16_t* dact, hipStream_t s);
+hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                                const int32_t* counts, const int32_t* tile_expert,
+                                const uint16_t* dact, const uint16_t* w1, uint16_t* dx_rows,
+                                hipStream_t s);
+hipError_t launch_gemm_wgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                                  const int32_t* counts, const uint16_t* dy_rows,
+                                  const uint16_t* h, uint16_t* dw2, hipStream_t s);
+hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
+                                const int32_t* counts, const uint16_t* dact,
+                                const uint16_t* x_rows, uint16_t* dw1, hipStream_t s);
+
+hipError_t launch_combine(int T, int H, int K, const uint16_t* y_rows, const int32_t* row_of,
+                          const float* topk_w, const uint16_t* y_shared, uint16_t* y,
+                          hipStream_t s);
+hipError_t launch_combine_bwd(int T, int H, int K, const uint16_t* dy, const uint16_t* y_rows,
+                              const int32_t* row_of, const float* topk_w, uint16_t* dy_rows,
+                              float* dg, hipStream_t s);
+hipError_t launch_unpermute_add(int T, int H, int K, const uint16_t* dx_rows,
+                                const int32_t* row_of, const uint16_t* dx_shared,
+                                const float* dx_router, uint16_t* dx, hipStream_t s);
+size_t route_bwd_workspace_bytes(int64_t m_cap, int H, int E);
+hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x_rows,
+                            const float* w_router, const int32_t* topk_idx, const float* topk_s,
+                            const float* dg, const int32_t* row_of, const int32_t* offsets,
+                            const int32_t* counts, float* dw_router, float* dx_router, void* ws,
+                            hipStream_t s);
+
+}  // namespace moe

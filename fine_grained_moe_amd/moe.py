@@ -1,0 +1,320 @@
+"""Thin Python binding of libmoe.so (the HIP library), same names as the C ABI.
+
+Only argument marshalling lives here: torch tensors are checked for dtype,
+device and contiguity, output tensors are allocated with torch (device memory
+is torch's job), and the raw pointers plus the current HIP stream are passed
+to the C entry points.  Every step of the layer runs in the library's HIP
+kernels; there is no fallback path.  Importing this module raises if the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m fine_grained_moe_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i32, _i64, _sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/moe.h
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_align": (_i32, []),
+    "moe_capacity_rows": (_i64, [_i32, _i32, _i32]),
+    "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_route": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_permute": (_i32, [_i32, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
+                           _p, _sz, _p]),
+    "moe_grouped_swiglu_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                      _p, _p]),
+    "moe_grouped_gate_up_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_down_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_combine": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "moe_combine_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_swiglu_bwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                      _p, _p, _p, _p, _p, _p]),
+    "moe_route_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                             _sz, _p]),
+    "moe_permute_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _check(status: int):
+    if status != 0:
+        msg = _lib.moe_last_error().decode()
+        raise MoEError(f"{_lib.moe_status_string(status).decode()} ({status}): {msg}")
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+BF16, F32, I32 = torch.bfloat16, torch.float32, torch.int32
+
+
+# ---------------------------------------------------------------------------
+# host queries
+# ---------------------------------------------------------------------------
+def moe_align() -> int:
+    return int(_lib.moe_align())
+
+
+def moe_capacity_rows(T: int, E: int, K: int) -> int:
+    return int(_lib.moe_capacity_rows(T, E, K))
+
+
+def moe_permute_workspace_bytes(T: int, E: int, K: int) -> int:
+    return int(_lib.moe_permute_workspace_bytes(T, E, K))
+
+
+def moe_route_bwd_workspace_bytes(T: int, H: int, E: int, K: int) -> int:
+    return int(_lib.moe_route_bwd_workspace_bytes(T, H, E, K))
+
+
+# ---------------------------------------------------------------------------
+# entry points (outputs allocated when not given)
+# ---------------------------------------------------------------------------
+def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None):
+    T, H = x.shape
+    E = w_router.shape[1]
+    dev = x.device
+    topk_idx = torch.empty((T, K), dtype=I32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, K), dtype=F32, device=dev) if topk_w is None else topk_w
+    topk_s = torch.empty((T, K), dtype=F32, device=dev) if topk_s is None else topk_s
+    _check(_lib.moe_route(T, H, E, K, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
+                          _ptr(bias, F32, "bias"), _ptr(topk_idx, I32, "topk_idx"),
+                          _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"), _stream()))
+    return topk_idx, topk_w, topk_s
+
+
+def moe_permute(topk_idx, x, E, m_cap=None, out=None, ws=None):
+    """Returns dict(counts, offsets, row_of, src_token, tile_expert, x_rows)."""
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    A = moe_align()
+    m_cap = moe_capacity_rows(T, E, K) if m_cap is None else m_cap
+    dev = x.device
+    if out is None:
+        out = dict(counts=torch.empty(E, dtype=I32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=I32, device=dev),
+                   row_of=torch.empty((T, K), dtype=I32, device=dev),
+                   src_token=torch.empty(m_cap, dtype=I32, device=dev),
+                   tile_expert=torch.empty(m_cap // A, dtype=I32, device=dev),
+                   x_rows=torch.empty((m_cap, H), dtype=BF16, device=dev))
+    nbytes = moe_permute_workspace_bytes(T, E, K)
+    if ws is None:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_permute(T, H, E, K, A, _ptr(topk_idx, I32, "topk_idx"), _ptr(x, BF16, "x"),
+                            m_cap, _ptr(out["counts"], I32), _ptr(out["offsets"], I32),
+                            _ptr(out["row_of"], I32), _ptr(out["src_token"], I32),
+                            _ptr(out["tile_expert"], I32), _ptr(out["x_rows"], BF16),
+                            _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def moe_grouped_swiglu_fwd(x_rows, w1, w2, offsets=None, counts=None, tile_expert=None,
+                           act=True, h=None, y_rows=None):
+    """Grouped SwiGLU FFN.  act=True allocates the saved pre-activations,
+    act=None skips them (inference), or pass a tensor.  Returns (act, h, y_rows)."""
+    M, H = x_rows.shape
+    G, twoF, H1 = w1.shape
+    F = twoF // 2
+    dev = x_rows.device
+    if act is True:
+        act = torch.empty((M, 2 * F), dtype=BF16, device=dev)
+    elif act is False:
+        act = None
+    h = torch.empty((M, F), dtype=BF16, device=dev) if h is None else h
+    y_rows = torch.empty((M, H), dtype=BF16, device=dev) if y_rows is None else y_rows
+    _check(_lib.moe_grouped_swiglu_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
+                                       _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
+                                       _ptr(w1, BF16, "w1"), _ptr(w2, BF16, "w2"),
+                                       _ptr(act, BF16, "act"), _ptr(h, BF16, "h"),
+                                       _ptr(y_rows, BF16, "y_rows"), _stream()))
+    return act, h, y_rows
+
+
+def moe_grouped_gate_up_fwd(x_rows, w1, offsets=None, counts=None, tile_expert=None, act=True,
+                            h=None):
+    """First half of moe_grouped_swiglu_fwd.  Returns (act, h)."""
+    M, H = x_rows.shape
+    G, twoF, _ = w1.shape
+    F = twoF // 2
+    dev = x_rows.device
+    if act is True:
+        act = torch.empty((M, 2 * F), dtype=BF16, device=dev)
+    elif act is False:
+        act = None
+    h = torch.empty((M, F), dtype=BF16, device=dev) if h is None else h
+    _check(_lib.moe_grouped_gate_up_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
+                                        _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
+                                        _ptr(w1, BF16, "w1"), _ptr(act, BF16, "act"),
+                                        _ptr(h, BF16, "h"), _stream()))
+    return act, h
+
+
+def moe_grouped_down_fwd(h, w2, offsets=None, counts=None, tile_expert=None, y_rows=None):
+    """Second half of moe_grouped_swiglu_fwd.  Returns y_rows."""
+    M, F = h.shape
+    G, H, _ = w2.shape
+    y_rows = torch.empty((M, H), dtype=BF16, device=h.device) if y_rows is None else y_rows
+    _check(_lib.moe_grouped_down_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
+                                     _ptr(tile_expert, I32), _ptr(h, BF16, "h"),
+                                     _ptr(w2, BF16, "w2"), _ptr(y_rows, BF16, "y_rows"),
+                                     _stream()))
+    return y_rows
+
+
+def moe_combine(y_rows, row_of, topk_w, y_shared=None, y=None):
+    T, K = row_of.shape
+    H = y_rows.shape[1]
+    y = torch.empty((T, H), dtype=BF16, device=y_rows.device) if y is None else y
+    _check(_lib.moe_combine(T, H, K, _ptr(y_rows, BF16, "y_rows"), _ptr(row_of, I32, "row_of"),
+                            _ptr(topk_w, F32, "topk_w"), _ptr(y_shared, BF16, "y_shared"),
+                            _ptr(y, BF16, "y"), _stream()))
+    return y
+
+
+def moe_combine_bwd(dy, y_rows, row_of, topk_w, dy_rows=None, dg=None):
+    T, K = row_of.shape
+    H = dy.shape[1]
+    dev = dy.device
+    if dy_rows is None:
+        dy_rows = torch.empty(y_rows.shape, dtype=BF16, device=dev)
+    dg = torch.empty((T, K), dtype=F32, device=dev) if dg is None else dg
+    _check(_lib.moe_combine_bwd(T, H, K, _ptr(dy, BF16, "dy"), _ptr(y_rows, BF16, "y_rows"),
+                                _ptr(row_of, I32, "row_of"), _ptr(topk_w, F32, "topk_w"),
+                                _ptr(dy_rows, BF16, "dy_rows"), _ptr(dg, F32, "dg"), _stream()))
+    return dy_rows, dg
+
+
+def moe_grouped_swiglu_bwd(x_rows, w1, w2, act, h, dy_rows, offsets=None, counts=None,
+                           tile_expert=None, dact=None, dx_rows=None, dw1=None, dw2=None):
+    """Returns (dact, dx_rows, dw1, dw2)."""
+    M, H = x_rows.shape
+    G, twoF, _ = w1.shape
+    F = twoF // 2
+    dev = x_rows.device
+    dact = torch.empty((M, 2 * F), dtype=BF16, device=dev) if dact is None else dact
+    dx_rows = torch.empty((M, H), dtype=BF16, device=dev) if dx_rows is None else dx_rows
+    dw1 = torch.empty(w1.shape, dtype=BF16, device=dev) if dw1 is None else dw1
+    dw2 = torch.empty(w2.shape, dtype=BF16, device=dev) if dw2 is None else dw2
+    _check(_lib.moe_grouped_swiglu_bwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
+                                       _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
+                                       _ptr(w1, BF16, "w1"), _ptr(w2, BF16, "w2"),
+                                       _ptr(act, BF16, "act"), _ptr(h, BF16, "h"),
+                                       _ptr(dy_rows, BF16, "dy_rows"), _ptr(dact, BF16, "dact"),
+                                       _ptr(dx_rows, BF16, "dx_rows"), _ptr(dw1, BF16, "dw1"),
+                                       _ptr(dw2, BF16, "dw2"), _stream()))
+    return dact, dx_rows, dw1, dw2
+
+
+def moe_route_bwd(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, counts,
+                  dw_router=None, dx_router=None, ws=None):
+    """Returns (dw_router [H,E] fp32, dx_router [T,H] fp32)."""
+    T, K = topk_idx.shape
+    H, E = w_router.shape
+    dev = w_router.device
+    dw_router = torch.empty((H, E), dtype=F32, device=dev) if dw_router is None else dw_router
+    dx_router = torch.empty((T, H), dtype=F32, device=dev) if dx_router is None else dx_router
+    nbytes = moe_route_bwd_workspace_bytes(T, H, E, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if ws is None else ws
+    _check(_lib.moe_route_bwd(T, H, E, K, _ptr(x_rows, BF16, "x_rows"),
+                              _ptr(w_router, F32, "w_router"), _ptr(topk_idx, I32, "topk_idx"),
+                              _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
+                              _ptr(row_of, I32, "row_of"), _ptr(offsets, I32, "offsets"),
+                              _ptr(counts, I32, "counts"), _ptr(dw_router, F32, "dw_router"),
+                              _ptr(dx_router, F32, "dx_router"), _ptr(ws), ws.numel(), _stream()))
+    return dw_router, dx_router
+
+
+def moe_permute_bwd(dx_rows, row_of, dx_shared=None, dx_router=None, dx=None):
+    T, K = row_of.shape
+    H = dx_rows.shape[1]
+    dx = torch.empty((T, H), dtype=BF16, device=dx_rows.device) if dx is None else dx
+    _check(_lib.moe_permute_bwd(T, H, K, _ptr(dx_rows, BF16, "dx_rows"), _ptr(row_of, I32, "row_of"),
+                                _ptr(dx_shared, BF16, "dx_shared"), _ptr(dx_router, F32, "dx_router"),
+                                _ptr(dx, BF16, "dx"), _stream()))
+    return dx
+
+
+# ---------------------------------------------------------------------------
+# the whole layer, composed from the entry points above
+# ---------------------------------------------------------------------------
+def fuse_shared(w1_sh, w2_sh):
+    """[S,2F,H] / [S,H,F] shared experts -> one expert of width S*F:
+    w1 = the S gate blocks, then the S up blocks ([1,2SF,H]); w2 = the S down
+    matrices side by side ([1,H,SF])."""
+    S, twoF, H = w1_sh.shape
+    F = twoF // 2
+    w1f = torch.cat([w1_sh[:, :F].reshape(S * F, H), w1_sh[:, F:].reshape(S * F, H)], 0)
+    w2f = torch.cat([w2_sh[s] for s in range(S)], 1)
+    return w1f.unsqueeze(0).contiguous(), w2f.unsqueeze(0).contiguous()
+
+
+def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backward=True):
+    """Forward of the MoE layer.  w1_shf / w2_shf are the fused shared weights
+    (fuse_shared), or None for no shared experts.  Returns (y, ctx)."""
+    E = w1.shape[0]
+    topk_idx, topk_w, topk_s = moe_route(x, w_router, bias, K)
+    p = moe_permute(topk_idx, x, E)
+    act, h, y_rows = moe_grouped_swiglu_fwd(p["x_rows"], w1, w2, p["offsets"], p["counts"],
+                                            p["tile_expert"], act=save_for_backward)
+    y_sh = act_sh = h_sh = None
+    if w1_shf is not None:
+        act_sh, h_sh, y_sh = moe_grouped_swiglu_fwd(x, w1_shf, w2_shf, act=save_for_backward)
+    y = moe_combine(y_rows, p["row_of"], topk_w, y_sh)
+    ctx = dict(x=x, w_router=w_router, w1=w1, w2=w2, w1_shf=w1_shf, w2_shf=w2_shf,
+               topk_idx=topk_idx, topk_w=topk_w, topk_s=topk_s, perm=p, act=act, h=h,
+               y_rows=y_rows, y_sh=y_sh, act_sh=act_sh, h_sh=h_sh)
+    return y, ctx
+
+
+def layer_backward(dy, ctx):
+    """Backward of the MoE layer.  Returns dict(dx, dw1, dw2, dw1_sh, dw2_sh,
+    dw_router) plus the intermediates."""
+    p = ctx["perm"]
+    dy_rows, dg = moe_combine_bwd(dy, ctx["y_rows"], p["row_of"], ctx["topk_w"])
+    dact, dx_rows, dw1, dw2 = moe_grouped_swiglu_bwd(p["x_rows"], ctx["w1"], ctx["w2"], ctx["act"],
+                                                     ctx["h"], dy_rows, p["offsets"], p["counts"],
+                                                     p["tile_expert"])
+    dx_sh = dw1_sh = dw2_sh = None
+    if ctx["w1_shf"] is not None:
+        _, dx_sh, dw1_sh, dw2_sh = moe_grouped_swiglu_bwd(ctx["x"], ctx["w1_shf"], ctx["w2_shf"],
+                                                          ctx["act_sh"], ctx["h_sh"], dy)
+    dw_router, dx_router = moe_route_bwd(p["x_rows"], ctx["w_router"], ctx["topk_idx"],
+                                         ctx["topk_s"], dg, p["row_of"], p["offsets"], p["counts"])
+    dx = moe_permute_bwd(dx_rows, p["row_of"], dx_sh, dx_router)
+    return dict(dx=dx, dw1=dw1, dw2=dw2, dw1_sh=dw1_sh, dw2_sh=dw2_sh, dw_router=dw_router,
+                dg=dg, dy_rows=dy_rows, dact=dact, dx_rows=dx_rows, dx_shared=dx_sh,
+                dx_router=dx_router)

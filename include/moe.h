@@ -1,0 +1,247 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) fine-grained MoE FFN layer library.
+ *
+ * The layer is the dots.llm1 mixture-of-experts feed-forward block:
+ *   - FP32 gating over E routed experts with a per-expert selection bias,
+ *     top-K selection, plus S always-on shared experts
+ *     ("dots.llm1 Technical Report" summary page, sections "Key claims" and
+ *     "Method"; "dots.llm1: the first MoE large language model open-sourced by
+ *     Little Red Book", section "Model Architecture Features");
+ *   - tokens permuted into per-expert segments padded to the GEMM tile
+ *     multiple, no token dropped (Technical Report summary, "Key claims" and
+ *     "Method");
+ *   - SwiGLU experts, each a two-layer feed-forward network (aibase news item,
+ *     architecture paragraph);
+ *   - the weighted combine of the K routed outputs plus the shared outputs.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless a comment says "host".  bf16 values
+ *     are passed as uint16_t bit patterns.  Every array is dense row-major.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory on these paths, never frees, and keeps no pointer after return.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and performs no host<->device synchronisation.
+ *   - Errors are reported by the return code only (moe_status_t); nothing is
+ *     thrown across the ABI.  Argument checks run on the host before any HIP
+ *     call, so a rejected call has launched nothing.  T == 0 is a valid no-op.
+ *   - Outputs are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics anywhere).
+ *   - Shape limits: H % 64 == 0, F % 32 == 0, 1 <= K <= E <= 128, K <= 16,
+ *     align == moe_align(); row counts below 2^31.
+ *
+ * Readings of what the pages leave open (all entry points follow them):
+ *   scores are sigmoid(logit); the bias is added for selection only; the K
+ *   combine weights are the selected scores normalised to sum 1; shared experts
+ *   have weight 1; ties in top-K go to the lower expert index (NaN ranks
+ *   lowest); the K experts of a token are listed by key descending; rows of a
+ *   segment are its tokens in ascending order; an expert with no tokens owns no
+ *   rows; gate = first F rows of W1 and h = silu(gate) * up; the backward is
+ *   the gradient with the routing decision held fixed (no bias gradient).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARGUMENT 1   /* null pointer, negative size, K > E ... */
+#define MOE_ERR_UNSUPPORTED_SHAPE 2  /* H, F, K, E or align outside the compiled limits */
+#define MOE_ERR_WORKSPACE_TOO_SMALL 3
+#define MOE_ERR_HIP 4                /* a HIP launch failed; see moe_last_error() */
+
+/* host: static string for a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* host: message of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* host: the segment alignment = the grouped-GEMM row tile (128). */
+int32_t moe_align(void);
+
+/* host: upper bound on the padded routed row count,
+ * ceil((T*K + E*(align-1)) / align) * align.  Row buffers of the routed path
+ * (x_rows, act, h, y_rows, dy_rows, dact, dx_rows) have this many rows. */
+int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K);
+
+/* host: bytes of the workspace moe_permute needs. */
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
+
+/* host: bytes of the workspace moe_route_bwd needs. */
+size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K);
+
+/*
+ * moe_route - FP32 gating, selection bias, top-K, combine weights.
+ * (Technical Report summary, "Method": gating projection in FP32, top-6 of 128,
+ * auxiliary-loss-free balancing by a bias; model card: dynamic bias terms.)
+ *
+ *   logit[t,e] = sum_h x[t,h] * w_router[h,e]         (fp32 arithmetic)
+ *   s[t,e]     = sigmoid(logit[t,e])
+ *   v[t,e]     = s[t,e] + bias[e]                      (selection key only)
+ *   topk_idx[t,:] = the K experts with the largest v, key descending, ties to
+ *                   the lower index
+ *   topk_s[t,k]   = s[t, topk_idx[t,k]]
+ *   topk_w[t,k]   = topk_s[t,k] / sum_j topk_s[t,j]
+ *
+ * x [T,H] bf16; w_router [H,E] fp32; bias [E] fp32;
+ * topk_idx [T,K] int32; topk_w [T,K] fp32; topk_s [T,K] fp32 (nullable).
+ */
+moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K,
+                       const uint16_t* x, const float* w_router, const float* bias,
+                       int32_t* topk_idx, float* topk_w, float* topk_s, void* stream);
+
+/*
+ * moe_permute - token permutation into per-expert segments padded to `align`
+ * rows (Technical Report summary, "Key claims" / "Method": segments padded to
+ * the GEMM tile multiple; no token dropped).  Integer outputs are bit-exact:
+ *
+ *   counts[e]      = number of tokens that selected e                    [E]
+ *   offsets[e]     = sum_{j<e} ceil(counts[j]/align)*align; offsets[E] is
+ *                    the padded total                                   [E+1]
+ *   row_of[t,k]    = offsets[e] + (number of tokens t' < t that selected
+ *                    e = topk_idx[t,k])                                  [T,K]
+ *   src_token[r]   = token held by row r, -1 for a padding row or a row
+ *                    at or beyond offsets[E]                             [m_cap]
+ *   tile_expert[i] = expert owning rows [i*align, (i+1)*align), -1 for
+ *                    tiles at or beyond offsets[E]                  [m_cap/align]
+ *   x_rows[r,:]    = x[src_token[r],:] for every non-padding row; padding rows
+ *                    are left untouched                            [m_cap,H] bf16
+ *
+ * topk_idx entries must lie in [0,E) and be distinct within a token (as
+ * moe_route writes them); other values are undefined behaviour.
+ * m_cap must be >= moe_capacity_rows(T,E,K) and a multiple of align.
+ * ws: device workspace of at least moe_permute_workspace_bytes(T,E,K) bytes.
+ */
+moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t align,
+                         const int32_t* topk_idx, const uint16_t* x, int64_t m_cap,
+                         int32_t* counts, int32_t* offsets, int32_t* row_of,
+                         int32_t* src_token, int32_t* tile_expert, uint16_t* x_rows,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu_fwd - grouped SwiGLU expert FFN over row segments
+ * (aibase news item: each expert is two feed-forward layers with SwiGLU;
+ * Technical Report summary: grouped GEMM over tile-padded expert segments).
+ *
+ * For every group g and every valid row r of its segment
+ * (offsets[g] <= r < offsets[g]+counts[g]):
+ *   [gate | up] = x_rows[r,:] . w1[g]^T      (w1 [G,2F,H]: gate rows 0..F-1)
+ *   h[r,:]      = silu(gate) * up            (bf16 [m_rows,F])
+ *   y_rows[r,:] = h[r,:] . w2[g]^T           (w2 [G,H,F]; bf16 [m_rows,H])
+ *   act[r,:]    = [gate | up] rounded to bf16 (bf16 [m_rows,2F]; nullable, kept
+ *                 for the backward)
+ * bf16 operands, fp32 accumulation, bf16 outputs.  Rows outside every
+ * segment are not written.
+ *
+ * Routed use: G = E, m_rows = m_cap, offsets/counts/tile_expert from
+ * moe_permute.  Dense use (the shared experts): offsets = counts =
+ * tile_expert = NULL, G = 1, m_rows = T: one segment of all T rows of x.  S
+ * shared experts are passed fused as one expert of width S*F: w1 = the S gate
+ * blocks stacked, then the S up blocks ([2SF,H]); w2 = the S down matrices side
+ * by side ([H,SF]); this equals the sum of the S experts.
+ */
+moe_status_t moe_grouped_swiglu_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* x_rows,
+                                    const uint16_t* w1, const uint16_t* w2, uint16_t* act,
+                                    uint16_t* h, uint16_t* y_rows, void* stream);
+
+/*
+ * moe_grouped_gate_up_fwd / moe_grouped_down_fwd - the two halves of
+ * moe_grouped_swiglu_fwd, same arguments and results: the first computes act
+ * and h (gate/up GEMM with SwiGLU fused into its epilogue), the second y_rows
+ * from h (down GEMM).  moe_grouped_swiglu_fwd is exactly the first followed by
+ * the second.
+ */
+moe_status_t moe_grouped_gate_up_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                     const int32_t* offsets, const int32_t* counts,
+                                     const int32_t* tile_expert, const uint16_t* x_rows,
+                                     const uint16_t* w1, uint16_t* act, uint16_t* h,
+                                     void* stream);
+moe_status_t moe_grouped_down_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                  const int32_t* offsets, const int32_t* counts,
+                                  const int32_t* tile_expert, const uint16_t* h,
+                                  const uint16_t* w2, uint16_t* y_rows, void* stream);
+
+/*
+ * moe_combine - weighted combine of the routed outputs plus the shared output
+ * (model card: 6 routed and 2 shared experts active per token):
+ *   y[t,:] = y_shared[t,:] + sum_k topk_w[t,k] * y_rows[row_of[t,k],:]
+ * fp32 accumulation in k order, one bf16 rounding.  y_shared nullable (zero).
+ * y_rows [*,H] bf16; row_of [T,K]; topk_w [T,K]; y_shared, y [T,H] bf16.
+ */
+moe_status_t moe_combine(int32_t T, int32_t H, int32_t K, const uint16_t* y_rows,
+                         const int32_t* row_of, const float* topk_w,
+                         const uint16_t* y_shared, uint16_t* y, void* stream);
+
+/*
+ * moe_combine_bwd - backward of moe_combine:
+ *   dy_rows[row_of[t,k],:] = topk_w[t,k] * dy[t,:]        (bf16)
+ *   dg[t,k]                = <dy[t,:], y_rows[row_of[t,k],:]>   (fp32)
+ * Padding rows of dy_rows are not written.
+ */
+moe_status_t moe_combine_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dy,
+                             const uint16_t* y_rows, const int32_t* row_of,
+                             const float* topk_w, uint16_t* dy_rows, float* dg,
+                             void* stream);
+
+/*
+ * moe_grouped_swiglu_bwd - backward of moe_grouped_swiglu_fwd with the same
+ * segment arguments (offsets/counts/tile_expert NULL = dense single group):
+ *   dh        = dy_rows . w2[g]                          (per valid row)
+ *   dgate     = dh * up * silu'(gate),  silu'(z) = sig(z)(1 + z(1 - sig(z)))
+ *   dup       = dh * silu(gate)
+ *   dact      = [dgate | dup]                            (bf16 [m_rows,2F])
+ *   dx_rows   = dact . w1[g]                             (bf16 [m_rows,H])
+ *   dw2[g]    = dy_rows_g^T . h_g                        (bf16 [G,H,F])
+ *   dw1[g]    = dact_g^T . x_rows_g                      (bf16 [G,2F,H])
+ * act and h are the forward's outputs.  Sums over rows run over the valid rows
+ * of the segment only; a group with no rows gets dw1[g] = dw2[g] = 0.
+ */
+moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* x_rows,
+                                    const uint16_t* w1, const uint16_t* w2,
+                                    const uint16_t* act, const uint16_t* h,
+                                    const uint16_t* dy_rows, uint16_t* dact,
+                                    uint16_t* dx_rows, uint16_t* dw1, uint16_t* dw2,
+                                    void* stream);
+
+/*
+ * moe_route_bwd - backward of moe_route's weights through the selected scores
+ * (routing decision held fixed, no bias gradient):
+ *   S_t        = sum_j topk_s[t,j],  g = topk_s / S_t
+ *   ds[t,k]    = (dg[t,k] - sum_j g[t,j] dg[t,j]) / S_t
+ *   dlogit[t,k]= ds[t,k] * s * (1 - s),   s = topk_s[t,k]
+ *   dw_router[h,e] = sum over tokens t that selected e of x[t,h] * dlogit   (fp32 [H,E])
+ *   dx_router[t,h] = sum_k dlogit[t,k] * w_router[h, topk_idx[t,k]]        (fp32 [T,H])
+ * The weight gradient is summed over expert segments, so it takes the
+ * permutation: x_rows, row_of, offsets, counts from moe_permute.
+ * ws: device workspace of at least moe_route_bwd_workspace_bytes(T,H,E,K).
+ */
+moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K,
+                           const uint16_t* x_rows, const float* w_router,
+                           const int32_t* topk_idx, const float* topk_s, const float* dg,
+                           const int32_t* row_of, const int32_t* offsets,
+                           const int32_t* counts, float* dw_router, float* dx_router,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_bwd - un-permute and add every path of the input gradient:
+ *   dx[t,:] = sum_k dx_rows[row_of[t,k],:] + dx_shared[t,:] + dx_router[t,:]
+ * fp32 accumulation, one bf16 rounding.  dx_shared (bf16) and dx_router (fp32)
+ * are nullable.
+ */
+moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx_rows,
+                             const int32_t* row_of, const uint16_t* dx_shared,
+                             const float* dx_router, uint16_t* dx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

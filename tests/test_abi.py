@@ -1,0 +1,132 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+answers the host queries, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "fine_grained_moe_amd", "libmoe.so")
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmoe.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ctypes.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+
+
+def test_binding_covers_every_symbol():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("moe_binding", os.path.join(ROOT, "fine_grained_moe_amd", "moe.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert sorted(mod.EXPORTED) == declared_functions()
+    for n in declared_functions():
+        if n not in ("moe_status_string", "moe_last_error"):
+            assert callable(getattr(mod, n)), n
+
+
+def test_host_queries(lib):
+    lib.moe_capacity_rows.restype = ctypes.c_int64
+    lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_status_string.restype = ctypes.c_char_p
+    assert lib.moe_align() == 128
+    # ceil((T*K + E*127)/128)*128
+    assert lib.moe_capacity_rows(8192, 128, 6) == 65408
+    assert lib.moe_capacity_rows(256, 128, 6) == 17792
+    assert lib.moe_capacity_rows(0, 8, 2) == 1024
+    assert lib.moe_capacity_rows(-1, 8, 2) == -1
+    assert lib.moe_permute_workspace_bytes(8192, 128, 6) == 2 * 32 * 128 * 4
+    assert lib.moe_permute_workspace_bytes(0, 128, 6) == 0
+    assert lib.moe_route_bwd_workspace_bytes(8192, 5120, 128, 6) == 128 * 5120 * 4 + 65408 * 4
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(3) == b"workspace too small"
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
+
+
+def test_route_rejects(lib):
+    f = lib.moe_route
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7
+    ok = [_p(FAKE)] * 6 + [_p(None)]
+    assert f(8, 64, 8, 9, *ok) == 1          # K > E
+    assert f(8, 64, 8, 0, *ok) == 1          # K = 0
+    assert f(-1, 64, 8, 2, *ok) == 1         # T < 0
+    assert f(8, 96, 8, 2, *ok) == 2          # H % 64
+    assert f(8, 64, 200, 2, *ok) == 2        # E > 128
+    assert f(8, 64, 32, 17, *ok) == 2        # K > 16
+    assert f(8, 64, 8, 2, _p(None), *[_p(FAKE)] * 5, _p(None)) == 1  # null x
+    assert f(0, 64, 8, 2, *[_p(None)] * 7) == 0   # T = 0 no-op
+    lib.moe_last_error.restype = ctypes.c_char_p
+    f(8, 64, 8, 9, *ok)
+    assert b"K > E" in lib.moe_last_error()
+
+
+def test_permute_rejects(lib):
+    f = lib.moe_permute
+    f.argtypes = ([ctypes.c_int32] * 5 + [ctypes.c_void_p] * 2 + [ctypes.c_int64] +
+                  [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p])
+    T, H, E, K = 100, 64, 8, 2
+    cap = 100 * 2 + 8 * 127
+    cap = (cap + 127) // 128 * 128
+    ptrs = [_p(FAKE)] * 2
+    outs = [_p(FAKE)] * 6
+    assert f(T, H, E, K, 64, *ptrs, cap, *outs, _p(FAKE), 1 << 20, _p(None)) == 2    # align
+    assert f(T, H, E, K, 128, *ptrs, cap - 128, *outs, _p(FAKE), 1 << 20, _p(None)) == 1  # m_cap
+    assert f(T, H, E, K, 128, *ptrs, cap + 1, *outs, _p(FAKE), 1 << 20, _p(None)) == 1   # not multiple
+    assert f(T, H, E, K, 128, *ptrs, cap, *outs, _p(FAKE), 4, _p(None)) == 3          # workspace
+    assert f(T, H, E, K, 128, _p(None), _p(FAKE), cap, *outs, _p(FAKE), 1 << 20, _p(None)) == 1
+
+
+def test_grouped_rejects(lib):
+    f = lib.moe_grouped_swiglu_fwd
+    f.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 10
+    w = [_p(FAKE)] * 7
+    assert f(4, 256, 64, 48, _p(FAKE), _p(FAKE), _p(FAKE), *w) == 2     # F % 32
+    assert f(4, 256, 100, 32, _p(FAKE), _p(FAKE), _p(FAKE), *w) == 2    # H % 64
+    assert f(4, 200, 64, 32, _p(FAKE), _p(FAKE), _p(FAKE), *w) == 1     # grouped rows % 128
+    assert f(2, 200, 64, 32, _p(None), _p(None), _p(None), *w) == 1     # dense with G != 1
+    assert f(1, 200, 64, 32, _p(FAKE), _p(None), _p(None), *w) == 1     # partial segment args
+    assert f(1, 0, 64, 32, _p(None), _p(None), _p(None), *w) == 0       # empty
+    g = lib.moe_grouped_swiglu_bwd
+    g.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 14
+    assert g(1, 128, 64, 32, _p(None), _p(None), _p(None), *[_p(FAKE)] * 9, _p(None), _p(None)) == 1
+
+
+def test_row_kernels_reject(lib):
+    for name, nptr in (("moe_combine", 6), ("moe_combine_bwd", 7), ("moe_permute_bwd", 6)):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * nptr
+        assert f(4, 64, 0, *[_p(FAKE)] * nptr) == 1
+        assert f(4, 60, 2, *[_p(FAKE)] * nptr) == 2
+        assert f(0, 64, 2, *[_p(None)] * nptr) == 0
+        assert f(4, 64, 2, *[_p(None)] * nptr) == 1
+
+
+def test_route_bwd_rejects(lib):
+    f = lib.moe_route_bwd
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 11, 16, _p(None)) == 3
+    assert f(16, 64, 8, 2, _p(None), *[_p(FAKE)] * 10, 1 << 30, _p(None)) == 1

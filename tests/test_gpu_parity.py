@@ -1,0 +1,365 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Small layers are compared element by element at every stage and end to end.
+The full dots.llm1-shaped workloads run in the launch configuration the
+benchmark times; there the oracle checks the complete routing and segment
+layout, whole expert segments of sampled experts, sampled tokens end to end,
+sampled hidden units of the shared experts, and the full router gradient.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from fine_grained_moe_amd.synthetic import WORKLOADS, Workload, generate_numpy, generate_torch
+from oracle import moe_oracle as O
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def M():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fine_grained_moe_amd import moe
+    return moe
+
+
+DEV = "cuda"
+ALIGN = 128
+
+
+@pytest.fixture(autouse=True)
+def _report():
+    """Print every comparison's errors (inf-norm, 2-norm, element-wise)."""
+    P.REPORT.clear()
+    yield
+    for name, e, n, el in P.REPORT:
+        print(f"  {name:40s} max {e:.2e}  norm {n:.2e}  elementwise {el:.2e}", flush=True)
+
+
+class LazyExperts:
+    """Per-expert fp32 view of a host bf16 tensor [E, R, C] (oracle input)."""
+
+    def __init__(self, t):
+        self.t = t.detach().to("cpu")
+        self.shape = tuple(self.t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].float().numpy()
+
+
+def unfuse_shared(dw1f, dw2f, S):
+    """Fused [2SF,H] / [H,SF] shared gradients -> per expert [S,2F,H] / [S,H,F]."""
+    twoSF, H = dw1f.shape
+    F = twoSF // (2 * S)
+    dw1 = np.stack([np.concatenate([dw1f[s * F:(s + 1) * F], dw1f[S * F + s * F:S * F + (s + 1) * F]])
+                    for s in range(S)])
+    dw2 = np.stack([dw2f[:, s * F:(s + 1) * F] for s in range(S)])
+    return dw1, dw2
+
+
+def to_gpu(inp):
+    t = {}
+    for k, v in inp.items():
+        if k in ("w_router", "bias"):
+            t[k] = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(DEV)
+        else:
+            t[k] = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(DEV).to(torch.bfloat16)
+    return t
+
+
+def run_layer(M, g, K, backward):
+    w1f, w2f = M.fuse_shared(g["w1_sh"], g["w2_sh"]) if g["w1_sh"].shape[0] > 0 else (None, None)
+    y, ctx = M.layer_forward(g["x"], g["w_router"], g["bias"], g["w1"], g["w2"], w1f, w2f, K)
+    grads = M.layer_backward(g["dy"], ctx) if backward else None
+    torch.cuda.synchronize()
+    return y, ctx, grads
+
+
+def full_layer_checks(M, inp, K, backward=True, label=""):
+    """Every stage and the whole layer against the full oracle (small layers)."""
+    E = inp["w1"].shape[0]
+    S = inp["w1_sh"].shape[0]
+    g = to_gpu(inp)
+    y, ctx, grads = run_layer(M, g, K, backward)
+    p = {k: P.to_np(v) for k, v in ctx["perm"].items()}
+    idx = P.to_np(ctx["topk_idx"])
+    m_cap = p["x_rows"].shape[0]
+
+    # routing
+    ref_route = O.route(inp["x"], inp["w_router"], inp["bias"], K)
+    n_diff, n_tie = P.check_route(idx, P.to_np(ctx["topk_w"]), P.to_np(ctx["topk_s"]), ref_route, label)
+    # segments, on the GPU's own routing (bit-exact)
+    ref_perm = O.permute(idx, E, ALIGN)
+    P.check_permute(p, ref_perm, E, ALIGN, m_cap)
+    valid = p["src_token"] >= 0
+    assert np.array_equal(p["x_rows"][valid], inp["x"][p["src_token"][valid]]), "x_rows"
+    # experts, on the GPU's own rows
+    x_rows = p["x_rows"]
+    act, hid, y_rows = O.experts_forward(x_rows, inp["w1"], inp["w2"], p["offsets"], p["counts"])
+    P.assert_close(f"{label} act", P.to_np(ctx["act"])[valid], act[valid])
+    P.assert_close(f"{label} h", P.to_np(ctx["h"])[valid], hid[valid])
+    P.assert_close(f"{label} y_rows", P.to_np(ctx["y_rows"])[valid], y_rows[valid])
+    y_sh = None
+    if S > 0:
+        y_sh_ref, _ = O.shared_forward(inp["x"], inp["w1_sh"], inp["w2_sh"])
+        y_sh = P.to_np(ctx["y_sh"])
+        P.assert_close(f"{label} y_shared", y_sh, y_sh_ref)
+    # combine, on the GPU's own rows and weights
+    y_comb = O.combine(P.to_np(ctx["y_rows"]), p["row_of"], P.to_np(ctx["topk_w"]), y_sh)
+    P.assert_close(f"{label} combine", P.to_np(y), y_comb)
+    # whole forward, on tokens whose routing agrees
+    ref_fwd = O.forward(inp, K, ALIGN)
+    same = np.all(idx == ref_fwd["route"]["topk_idx"], axis=1)
+    P.assert_close(f"{label} y", P.to_np(y)[same], ref_fwd["y"][same])
+    if not backward:
+        return dict(n_diff=n_diff, n_tie=n_tie)
+
+    dy = inp["dy"]
+    # combine backward, on the GPU's own rows
+    dy_rows_ref, dg_ref = O.combine_bwd(dy, P.to_np(ctx["y_rows"]), p["row_of"], P.to_np(ctx["topk_w"]), m_cap)
+    P.assert_close(f"{label} dy_rows", P.to_np(grads["dy_rows"])[valid], dy_rows_ref[valid])
+    P.assert_close(f"{label} dg", P.to_np(grads["dg"]), dg_ref)
+    # expert backward, on the GPU's own rows and upstream rows
+    dx_rows_ref, dW1_ref, dW2_ref, dact_ref = O.experts_backward(
+        x_rows, inp["w1"], inp["w2"], act, P.to_np(grads["dy_rows"]), p["offsets"], p["counts"])
+    P.assert_close(f"{label} dact", P.to_np(grads["dact"])[valid], dact_ref[valid])
+    P.assert_close(f"{label} dx_rows", P.to_np(grads["dx_rows"])[valid], dx_rows_ref[valid])
+    P.per_slice_close(f"{label} dW1", P.to_np(grads["dw1"]), dW1_ref)
+    P.per_slice_close(f"{label} dW2", P.to_np(grads["dw2"]), dW2_ref)
+    if S > 0:
+        dW1s, dW2s = unfuse_shared(P.to_np(grads["dw1_sh"])[0], P.to_np(grads["dw2_sh"])[0], S)
+        for s in range(S):
+            a, _, _ = O.expert_ffn(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s])
+            _, dw1r, dw2r, _ = O.expert_ffn_bwd(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s], a, dy)
+            P.assert_close(f"{label} dW1_sh[{s}]", dW1s[s], dw1r)
+            P.assert_close(f"{label} dW2_sh[{s}]", dW2s[s], dw2r)
+    # router backward, on the GPU's own routing and dg
+    dWr_ref, dxr_ref, _ = O.router_bwd(inp["x"], inp["w_router"], idx, P.to_np(ctx["topk_s"]),
+                                        P.to_np(grads["dg"]))
+    P.assert_close(f"{label} dW_r", P.to_np(grads["dw_router"]), dWr_ref)
+    P.assert_close(f"{label} dx_router", P.to_np(grads["dx_router"]), dxr_ref)
+    # un-permute-add, on the GPU's own terms
+    extra = [P.to_np(grads["dx_router"])]
+    if S > 0:
+        extra.append(P.to_np(grads["dx_shared"]))
+    dx_un = O.unpermute_add(P.to_np(grads["dx_rows"]), p["row_of"], extra)
+    P.assert_close(f"{label} dx (un-permute)", P.to_np(grads["dx"]), dx_un)
+    # whole backward against the oracle's own forward and backward
+    ref_bwd = O.backward(inp, ref_fwd, dy)
+    P.assert_close(f"{label} dx", P.to_np(grads["dx"])[same], ref_bwd["dx"][same])
+    if same.all():
+        P.per_slice_close(f"{label} dW1 (e2e)", P.to_np(grads["dw1"]), ref_bwd["dW1"])
+        P.per_slice_close(f"{label} dW2 (e2e)", P.to_np(grads["dw2"]), ref_bwd["dW2"])
+        P.assert_close(f"{label} dW_r (e2e)", P.to_np(grads["dw_router"]), ref_bwd["dW_r"])
+    return dict(n_diff=n_diff, n_tie=n_tie)
+
+
+# ---------------------------------------------------------------------------
+# small layers: every stage, element by element
+# ---------------------------------------------------------------------------
+def test_tiny_workload(M):
+    w = WORKLOADS["tiny"]
+    inp = generate_numpy(w.with_(all_fp32=False), with_dy=True)  # GPU takes bf16 x / W1 / W2
+    full_layer_checks(M, inp, w.K, label="tiny")
+
+
+MID = {
+    # several row tiles per expert, ragged tails, ragged N tiles (F=352), E=16
+    "T1000_H512_E16_K4_F352": Workload("mid", T=1000, H=512, E=16, K=4, S=2, F=352, seed=21,
+                                       router_std=0.08, bias_std=0.05),
+    # dots-like expert count with small hidden size
+    "T777_H256_E128_K6_F96": Workload("mid2", T=777, H=256, E=128, K=6, S=2, F=96, seed=22,
+                                      router_std=0.1),
+    # skewed: a Zipf bias concentrates tokens on few experts, most experts empty
+    "T1500_H256_E64_K6_F64_skew": Workload("skew-small", T=1500, H=256, E=64, K=6, S=1, F=64,
+                                           seed=23, bias_kind="zipf", router_std=0.02),
+    # K = 1, no shared expert
+    "T300_H128_E8_K1_S0": Workload("k1", T=300, H=128, E=8, K=1, S=0, F=64, seed=24,
+                                   router_std=0.1),
+    # K = E: every expert selected by every token
+    "T200_H128_E4_K4": Workload("keqe", T=200, H=128, E=4, K=4, S=1, F=128, seed=25,
+                                router_std=0.1),
+    # a single token
+    "T1_H256_E32_K6": Workload("t1", T=1, H=256, E=32, K=6, S=2, F=64, seed=26, router_std=0.1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MID))
+def test_small_layers(M, name):
+    w = MID[name]
+    inp = generate_numpy(w, with_dy=True)
+    full_layer_checks(M, inp, w.K, label=name)
+
+
+def test_skew_has_empty_experts_with_zero_grad(M):
+    w = MID["T1500_H256_E64_K6_F64_skew"]
+    inp = generate_numpy(w, with_dy=True)
+    g = to_gpu(inp)
+    y, ctx, grads = run_layer(M, g, w.K, True)
+    counts = P.to_np(ctx["perm"]["counts"])
+    empty = np.nonzero(counts == 0)[0]
+    assert len(empty) > 10
+    dw1 = P.to_np(grads["dw1"])
+    dw2 = P.to_np(grads["dw2"])
+    assert (dw1[empty] == 0).all() and (dw2[empty] == 0).all()
+    assert (P.to_np(grads["dw_router"])[:, empty] == 0).all()
+
+
+def test_deterministic(M):
+    w = MID["T1000_H512_E16_K4_F352"]
+    inp = generate_numpy(w, with_dy=True)
+    g = to_gpu(inp)
+    outs = []
+    for _ in range(2):
+        y, ctx, grads = run_layer(M, g, w.K, True)
+        outs.append([y.clone(), grads["dx"].clone(), grads["dw1"].clone(), grads["dw2"].clone(),
+                     grads["dw_router"].clone(), ctx["topk_idx"].clone(), ctx["perm"]["row_of"].clone()])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_empty_batch(M):
+    E, K, H, F = 8, 2, 64, 32
+    x = torch.zeros((0, H), dtype=torch.bfloat16, device=DEV)
+    wr = torch.randn((H, E), device=DEV)
+    b = torch.zeros(E, device=DEV)
+    w1 = torch.randn((E, 2 * F, H), device=DEV).to(torch.bfloat16)
+    w2 = torch.randn((E, H, F), device=DEV).to(torch.bfloat16)
+    idx, tw, ts = M.moe_route(x, wr, b, K)
+    p = M.moe_permute(idx, x, E)
+    torch.cuda.synchronize()
+    assert (p["counts"] == 0).all() and (p["offsets"] == 0).all()
+    assert (p["tile_expert"] == -1).all() and (p["src_token"] == -1).all()
+    act, h, yr = M.moe_grouped_swiglu_fwd(p["x_rows"], w1, w2, p["offsets"], p["counts"], p["tile_expert"])
+    dy_rows = torch.zeros_like(yr)
+    _, _, dw1, dw2 = M.moe_grouped_swiglu_bwd(p["x_rows"], w1, w2, act, h, dy_rows, p["offsets"],
+                                              p["counts"], p["tile_expert"])
+    dg = torch.zeros((0, K), device=DEV)
+    dwr, dxr = M.moe_route_bwd(p["x_rows"], wr, idx, ts, dg, p["row_of"], p["offsets"], p["counts"])
+    torch.cuda.synchronize()
+    assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# full dots.llm1-shaped workloads (the benchmark's launch configuration)
+# ---------------------------------------------------------------------------
+def sampled_checks(M, w, backward, n_tokens=12, seed=0):
+    g = generate_torch(w, DEV, with_dy=backward)
+    K, E, S = w.K, w.E, w.S
+    y, ctx, grads = run_layer(M, g, K, backward)
+    x = P.to_np(g["x"])
+    wr = P.to_np(g["w_router"])
+    bias = P.to_np(g["bias"])
+    W1, W2 = LazyExperts(g["w1"]), LazyExperts(g["w2"])
+    W1s, W2s = P.to_np(g["w1_sh"]), P.to_np(g["w2_sh"])
+
+    # full routing and segments
+    idx = P.to_np(ctx["topk_idx"])
+    ref_route = O.route(x, wr, bias, K)
+    n_diff, n_tie = P.check_route(idx, P.to_np(ctx["topk_w"]), P.to_np(ctx["topk_s"]), ref_route, w.name)
+    print(f"[{w.name}] routing: {n_diff} tokens differ, {n_tie} near-ties", flush=True)
+    p = {k: P.to_np(v) for k, v in ctx["perm"].items() if k != "x_rows"}
+    ref_perm = O.permute(idx, E, ALIGN)
+    P.check_permute(p, ref_perm, E, ALIGN, p["src_token"].shape[0])
+    src = torch.from_numpy(p["src_token"]).to(DEV).long()
+    vmask = src >= 0
+    assert torch.equal(ctx["perm"]["x_rows"][vmask], g["x"][src[vmask]]), "x_rows"
+
+    # whole expert segments of sampled experts (stage-wise, GPU rows)
+    counts = p["counts"]
+    nonempty = np.nonzero(counts)[0]
+    pick = sorted({int(nonempty[0]), int(nonempty[-1]), int(nonempty[len(nonempty) // 2]),
+                   int(np.argmax(counts))})
+    rng = np.random.default_rng(seed)
+    for e in pick:
+        r0, n = int(p["offsets"][e]), int(counts[e])
+        if n > 2048:  # bound host work on giant segments: a random row subset
+            rows = np.sort(rng.choice(n, 2048, replace=False)) + r0
+        else:
+            rows = np.arange(r0, r0 + n)
+        xr = P.to_np(ctx["perm"]["x_rows"][torch.from_numpy(rows).to(DEV)])
+        a, hid, ye = O.expert_ffn(xr, W1[e], W2[e])
+        sel = torch.from_numpy(rows).to(DEV)
+        P.assert_close(f"{w.name} act[e={e}]", P.to_np(ctx["act"][sel]), a)
+        P.assert_close(f"{w.name} h[e={e}]", P.to_np(ctx["h"][sel]), hid)
+        P.assert_close(f"{w.name} y_rows[e={e}]", P.to_np(ctx["y_rows"][sel]), ye)
+
+    # sampled tokens end to end (routing agreeing)
+    toks = np.sort(rng.choice(w.T, n_tokens, replace=False))
+    sub = dict(x=x[toks], w_router=wr, bias=bias, w1=W1, w2=W2, w1_sh=W1s, w2_sh=W2s)
+    ref = O.forward(sub, K, ALIGN)
+    same = np.all(idx[toks] == ref["route"]["topk_idx"], axis=1)
+    P.assert_close(f"{w.name} y[sampled]", P.to_np(y)[toks][same], ref["y"][same])
+    if not backward:
+        return
+    dy = P.to_np(g["dy"])
+    sub["dy"] = dy[toks]
+    ref_b = O.backward(sub, ref, sub["dy"])
+    P.assert_close(f"{w.name} dx[sampled]", P.to_np(grads["dx"])[toks][same], ref_b["dx"][same])
+    P.assert_close(f"{w.name} dg[sampled]", P.to_np(grads["dg"])[toks][same], ref_b["dg"][same])
+
+    # expert weight gradients of sampled experts (stage-wise, GPU upstream rows)
+    for e in pick[:3]:
+        r0, n = int(p["offsets"][e]), int(counts[e])
+        if n > 4096:
+            continue
+        sel = torch.arange(r0, r0 + n, device=DEV)
+        xr = P.to_np(ctx["perm"]["x_rows"][sel])
+        a, _, _ = O.expert_ffn(xr, W1[e], W2[e])
+        dxr, dw1r, dw2r, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, P.to_np(grads["dy_rows"][sel]))
+        P.assert_close(f"{w.name} dact[e={e}]", P.to_np(grads["dact"][sel]), dar)
+        P.assert_close(f"{w.name} dx_rows[e={e}]", P.to_np(grads["dx_rows"][sel]), dxr)
+        P.assert_close(f"{w.name} dW1[e={e}]", P.to_np(grads["dw1"][e]), dw1r)
+        P.assert_close(f"{w.name} dW2[e={e}]", P.to_np(grads["dw2"][e]), dw2r)
+    empty = np.nonzero(counts == 0)[0]
+    if len(empty):
+        assert not grads["dw1"][torch.from_numpy(empty).to(DEV)].any()
+        assert not grads["dw2"][torch.from_numpy(empty).to(DEV)].any()
+
+    # shared experts: sampled hidden units (each unit's gradient depends on it alone)
+    F = w.F
+    dw1f = grads["dw1_sh"][0]
+    dw2f = grads["dw2_sh"][0]
+    for s in range(S):
+        for f in rng.choice(F, 3, replace=False):
+            w1u = W1s[s][[f, F + f]]
+            w2u = W2s[s][:, [f]]
+            au, _, _ = O.expert_ffn(x, w1u, w2u)
+            _, dw1u, dw2u, _ = O.expert_ffn_bwd(x, w1u, w2u, au, dy)
+            gate_row, up_row = s * F + f, S * F + s * F + f
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] gate", P.to_np(dw1f[gate_row]), dw1u[0])
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] up", P.to_np(dw1f[up_row]), dw1u[1])
+            P.assert_close(f"{w.name} dW2_sh[{s},{f}]", P.to_np(dw2f[:, s * F + f]), dw2u[:, 0])
+
+    # router gradient, full, on the GPU's own routing and dg
+    dWr_ref, _, _ = O.router_bwd(x, wr, idx, P.to_np(ctx["topk_s"]), P.to_np(grads["dg"]))
+    P.assert_close(f"{w.name} dW_r", P.to_np(grads["dw_router"]), dWr_ref)
+
+
+@pytest.mark.timeout(600)
+def test_decode_full_oracle(M):
+    """T=256 at dots shapes: small enough for the whole oracle."""
+    w = WORKLOADS["decode"]
+    g = generate_torch(w, DEV, with_dy=True)
+    inp = {k: P.to_np(v) for k, v in g.items()}
+    full_layer_checks(M, inp, w.K, backward=True, label="decode")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_sampled(M):
+    sampled_checks(M, WORKLOADS["prefill"], backward=False)
+
+
+@pytest.mark.timeout(600)
+def test_skew_sampled(M):
+    sampled_checks(M, WORKLOADS["skew"], backward=True)
+
+
+@pytest.mark.timeout(600)
+def test_fwdbwd_sampled(M):
+    sampled_checks(M, WORKLOADS["fwdbwd"], backward=True)
