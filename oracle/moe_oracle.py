@@ -116,6 +116,20 @@ def near_tie_mask(keys, K):
     return rel < NEAR_TIE_REL
 
 
+def order_tie_mask(keys, K):
+    """Tokens with two adjacent ranks among their K selected keys closer than
+    NEAR_TIE_REL relative: the order of those two experts in the token's list
+    may legitimately differ between two correct fp32 evaluations."""
+    v = np.asarray(keys, F64)
+    v = np.where(np.isnan(v), -np.inf, v)
+    srt = -np.sort(-v, axis=1)[:, :K]
+    if K < 2:
+        return np.zeros(v.shape[0], bool)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = (srt[:, :-1] - srt[:, 1:]) / np.abs(srt[:, :-1])
+    return np.any(rel < NEAR_TIE_REL, axis=1)
+
+
 def route(x, w_router, bias, K):
     """Whole routing step: logits, scores, keys, top-K, combine weights."""
     logits = router_logits(x, w_router)
@@ -125,7 +139,7 @@ def route(x, w_router, bias, K):
     return dict(logits=logits, scores=s, keys=v, topk_idx=idx,
                 topk_w=combine_weights(s, idx),
                 topk_s=np.take_along_axis(s, idx.astype(np.int64), axis=1),
-                near_tie=near_tie_mask(v, K))
+                near_tie=near_tie_mask(v, K), order_tie=order_tie_mask(v, K))
 
 
 # ---------------------------------------------------------------------------

@@ -67,6 +67,15 @@ def test_near_tie_mask():
     assert not O.near_tie_mask(keys, 4).any()
 
 
+def test_order_tie_mask():
+    keys = np.array([[0.9, 0.9 * (1 - 3e-7), 0.5, 0.1],     # ranks 1 and 2 nearly equal
+                     [0.9, 0.8, 0.5, 0.5 * (1 - 3e-7)],     # tie only past rank K=3
+                     [0.9, 0.8, 0.5, 0.1]], np.float32)
+    assert O.order_tie_mask(keys, 3).tolist() == [True, False, False]
+    assert O.near_tie_mask(keys, 3).tolist() == [False, True, False]
+    assert not O.order_tie_mask(keys, 1).any()
+
+
 def test_permute_golden():
     P.check_permute_golden(O)
 
