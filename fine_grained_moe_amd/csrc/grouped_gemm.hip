@@ -5,8 +5,14 @@
 // ("dots.llm1 Technical Report" summary page, "Key claims" and "Method": the
 // grouped GEMM pads expert token segments to tile multiples so tiling inside a
 // block is uniform).  The pages built that for Hopper WGMMA tiles; here the
-// tile is sized for CDNA4: a 128x256 workgroup tile of four wave64 waves, each
-// computing 64x128 with v_mfma_f32_32x32x16_bf16, LDS double-buffered.
+// tiles are sized for CDNA4 (v_mfma_f32_32x32x16_bf16, wave64, 160 KB LDS):
+//   row-grouped products (rows = expert segments, 128-row aligned):
+//     128 x 256 x 64 workgroup tile, 8 waves (2 per SIMD) of 64 x 64, 3 stages
+//   weight gradients and the dense shared-expert products:
+//     256 x 256 x 32 workgroup tile, 8 waves of 128 x 64, 4 stages
+// Operands move global -> LDS with buffer_load ... lds (no VGPR staging),
+// issued interleaved with the MFMAs of the current stage; a 3- or 4-deep LDS
+// ring keeps two or three stages in flight.
 //
 // One kernel template covers the six products of the layer:
 //   forward  gate/up  x_rows[M,H] . W1_e^T   (A K-contig, B K-contig) + SwiGLU epilogue
@@ -17,11 +23,13 @@
 //   backward wgrad    dact_e^T    . x_rows_e (both M/N-contig, K = segment rows)
 //
 // LDS operand layouts (bf16):
-//   K-contig tile  [rows][64 k]: 128 B per row, 16 B chunk c stored at
-//                  c ^ ((row >> 1) & 7).  Fragments read with ds_read_b128.
-//   MN-contig tile [64 k][cols]: 2*cols B per k-row, 16 B chunk c stored at
+//   K-contig tile  [rows][BK k]: 2*BK B per row; 16 B chunk c stored at
+//                  c ^ ((row >> 1) & 7) (BK = 64) or c ^ ((row >> 2) & 3)
+//                  (BK = 32).  Fragments read with ds_read_b128.
+//   MN-contig tile [BK k][cols]: 2*cols B per k-row, 16 B chunk c stored at
 //                  c ^ (4 * (k & 3)).  Fragments read with two
 //                  ds_read_b64_tr_b16 (transposing LDS read of gfx950).
+// Both layouts are free of LDS bank conflicts for these reads.
 // Both give the same MFMA fragment: lane l holds Op[mn = base + l%32]
 // [k = 16*kk + 8*(l/32) + 0..7].
 //
@@ -35,7 +43,41 @@
 namespace moe {
 namespace gemm {
 
-constexpr int BM = 128, BN = 256, BK = 64, NT = 256;
+template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NW = WGM * WGN, NT = NW * 64;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  static constexpr int WM = WTM / 32, WN = WTN / 32;    // 32x32 MFMA blocks per wave
+  static constexpr int KK = BK / 16;                    // MFMA k-steps per stage
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+};
+// Tile depth and pipeline depth are build-time tunables (defaults measured best).
+#ifndef MOE_ROWS_BK
+#define MOE_ROWS_BK 64
+#endif
+#ifndef MOE_ROWS_STAGES
+#define MOE_ROWS_STAGES 3
+#endif
+#ifndef MOE_WIDE_BK
+#define MOE_WIDE_BK 32
+#endif
+#ifndef MOE_WIDE_STAGES
+#define MOE_WIDE_STAGES 4
+#endif
+// row-grouped tile order: 1 = expert-major (all m-tiles of one expert and one
+// n-tile adjacent, then the next n-tile of the same expert); 0 = groups of
+// GROUP_M m-tiles regardless of expert boundaries
+#ifndef MOE_EXPERT_MAJOR
+#define MOE_EXPERT_MAJOR 1
+#endif
+using CfgRows = TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, 2, 4>;  // 128-row expert segments
+using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4>;  // weight grads, dense expert
+static_assert(CfgRows::LDS_BYTES <= 160 * 1024 && CfgWide::LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
+
 constexpr int GROUP_M = 4;  // m-tiles per rasterization group
 
 enum Src { KC = 0, MC = 1 };
@@ -51,7 +93,7 @@ struct Args {
   const int32_t* offsets;
   const int32_t* counts;
   const int32_t* tile_expert;
-  int64_t m_rows;        // MGROUP: rows of A/C; KGROUP dense: rows of the segment
+  int64_t m_rows;        // MGROUP: rows of A/C; dense KGROUP: rows of the segment
   int M, N, K;           // logical GEMM dims (MGROUP: M unused; KGROUP: per group)
   int lda, ldb, ldc;     // leading dims (elements)
   int64_t strideB;       // elements between consecutive groups' B
@@ -61,84 +103,129 @@ struct Args {
 };
 
 // --------------------------------------------------------------------------
-// Global -> register staging of one BK slice of an operand tile
+// Global -> LDS: buffer loads straight into LDS (buffer_load_dwordx4 ... lds)
 // --------------------------------------------------------------------------
-// K-contig tile of R rows: chunk q -> row q/8, k-chunk q%8.
-template <int R>
-struct KcStage {
-  static constexpr int PER = R * 8 / NT;
-  u32x4 v[PER];
-  // row_ptr(row) returns the global row pointer or nullptr if the row is invalid
-  template <class RowFn>
-  __device__ __forceinline__ void load(RowFn row_ptr, int k0, int K, int tid) {
+// Each wave-level load moves 64 lanes x 16 B = 1 KB into a contiguous LDS
+// region whose base is wave-uniform (M0); lane l lands at base + 16*l.  The
+// LDS swizzle is therefore applied on the global side: lane l fetches the
+// global chunk that belongs at its LDS slot.  A lane whose element is out of
+// range (rows past the segment, k past K, columns past N) gets an offset past
+// the buffer's num_records, which the hardware turns into zeros (checked per
+// dword), so masked rows and tails contribute exactly nothing.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) leaving expcnt/lgkmcnt unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// wait until at most `ahead` stages of LOADS loads each are still in flight
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXA <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAXA) wait_vmcnt<LOADS * MAXA>();
+    else wait_stages<LOADS, MAXA - 1>(ahead);
+  }
+}
+
+template <int BK>
+__device__ __forceinline__ int kc_swz(int r) {
+  return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+// K-contig tile of R rows x BK k.  A 1 KB region holds RPR consecutive rows.
+template <int R, int BK, int NW>
+struct KcLoad {
+  static constexpr int CPR = BK / 8;           // 16-byte chunks per row
+  static constexpr int RPR = 1024 / (BK * 2);  // rows per region
+  static constexpr int PER = R / RPR / NW;     // regions per wave
+  static_assert(PER * RPR * NW == R, "tile rows");
+  uint32_t off[PER];  // byte offset of the lane's chunk at kt = 0, or kOOB
+  int kel[PER];       // k offset (elements) of the lane's chunk within a stage
+  template <class RowOff>
+  __device__ __forceinline__ void init(RowOff row_off, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int q = tid + i * NT;
-      int r = q >> 3, c = q & 7;
-      const uint16_t* p = row_ptr(r);
-      int k = k0 + c * 8;
-      if (p != nullptr && k < K)
-        v[i] = *(const u32x4*)(p + k);
-      else
-        v[i] = u32x4{0, 0, 0, 0};
+      const int q = i * NW + wave;
+      const int r = q * RPR + lane / CPR;
+      const int c = (lane % CPR) ^ kc_swz<BK>(r);
+      const uint32_t ro = row_off(r);
+      off[i] = ro == kOOB ? kOOB : ro + c * 16;
+      kel[i] = c * 8;
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int q = tid + i * NT;
-      int r = q >> 3, c = q & 7;
-      *(u32x4*)(lds + r * 128 + ((c ^ ((r >> 1) & 7)) << 4)) = v[i];
-    }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int wave, int i,
+                                        int kt, int K) const {
+    const int q = i * NW + wave;
+    const bool kin = kt * BK + kel[i] < K;
+    const uint32_t v = (off[i] == kOOB || !kin) ? kOOB : off[i] + (uint32_t)kt * (BK * 2);
+    dma16(rs, lds + q * 1024, v);
   }
 };
 
-// MN-contig tile of C columns: chunk q -> k-row q/(C/8), col-chunk q%(C/8).
-template <int C>
-struct McStage {
-  static constexpr int CPR = C / 8;  // chunks per k-row
-  static constexpr int PER = BK * CPR / NT;
-  u32x4 v[PER];
-  // krow_ptr(k) returns the global pointer of k-row (at the tile's first col) or nullptr
-  template <class KRowFn>
-  __device__ __forceinline__ void load(KRowFn krow_ptr, int col0, int ncols, int tid) {
+// MN-contig tile of BK k-rows x C columns.  A 1 KB region holds KPR k-rows.
+template <int C, int BK, int NW>
+struct McLoad {
+  static constexpr int CPR = C / 8;           // chunks per k-row
+  static constexpr int KPR = 1024 / (2 * C);  // k-rows per region
+  static constexpr int PER = BK / KPR / NW;   // regions per wave
+  static_assert(PER * KPR * NW == BK, "tile k-rows");
+  uint32_t coff[PER];  // byte offset of the lane's column chunk, or kOOB
+  int kr[PER];         // k-row (0..BK-1) of the lane's chunk
+  template <class ColOff>
+  __device__ __forceinline__ void init(ColOff col_off, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int q = tid + i * NT;
-      int kr = q / CPR, c = q % CPR;
-      const uint16_t* p = krow_ptr(kr);
-      if (p != nullptr && col0 + c * 8 < ncols)
-        v[i] = *(const u32x4*)(p + c * 8);
-      else
-        v[i] = u32x4{0, 0, 0, 0};
+      const int q = i * NW + wave;
+      const int k = q * KPR + lane / CPR;
+      const int c = (lane % CPR) ^ (4 * (k & 3));
+      kr[i] = k;
+      coff[i] = col_off(c * 8);
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int q = tid + i * NT;
-      int kr = q / CPR, c = q % CPR;
-      *(u32x4*)(lds + kr * (C * 2) + ((c ^ (4 * (kr & 3))) << 4)) = v[i];
-    }
+  // krow_off(k) -> byte offset of global k-row k, or kOOB
+  template <class KRowOff>
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int wave, int i,
+                                        int kt, KRowOff krow_off) const {
+    const int q = i * NW + wave;
+    const uint32_t ko = krow_off(kt * BK + kr[i]);
+    const uint32_t v = (ko == kOOB || coff[i] == kOOB) ? kOOB : ko + coff[i];
+    dma16(rs, lds + q * 1024, v);
   }
 };
 
 // --------------------------------------------------------------------------
-// LDS -> fragment
+// LDS -> fragment: lane l gets Op[mn = base + l%32][k = 16*kk + 8*(l/32) + 0..7]
 // --------------------------------------------------------------------------
+template <int BK>
 __device__ __forceinline__ bf16x8 frag_kc(const uint8_t* lds, int base, int kk, int lane) {
-  int row = base + (lane & 31);
-  int c = 2 * kk + (lane >> 5);
-  return *(const bf16x8*)(lds + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+  const int row = base + (lane & 31);
+  const int c = 2 * kk + (lane >> 5);
+  return *(const bf16x8*)(lds + row * (BK * 2) + ((c ^ kc_swz<BK>(row)) << 4));
 }
 
 template <int C>
 __device__ __forceinline__ bf16x8 frag_mc(const uint8_t* lds, int base, int kk, int lane) {
-  int g = lane >> 4, li = lane & 15;
-  int col = base + 16 * (g & 1) + 4 * (li & 3);
-  int kb = 16 * kk + 8 * (g >> 1) + (li >> 2);
-  int c = col >> 3, sub = (col & 7) * 2;
-  int k0 = kb, k1 = kb + 4;
+  const int g = lane >> 4, li = lane & 15;
+  const int col = base + 16 * (g & 1) + 4 * (li & 3);
+  const int kb = 16 * kk + 8 * (g >> 1) + (li >> 2);
+  const int c = col >> 3, sub = (col & 7) * 2;
+  const int k0 = kb, k1 = kb + 4;
   const uint8_t* p0 = lds + k0 * (C * 2) + ((c ^ (4 * (k0 & 3))) << 4) + sub;
   const uint8_t* p1 = lds + k1 * (C * 2) + ((c ^ (4 * (k1 & 3))) << 4) + sub;
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p0));
@@ -148,45 +235,56 @@ __device__ __forceinline__ bf16x8 frag_mc(const uint8_t* lds, int base, int kk, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int SRC, int C>
+template <int SRC, int C, int BK>
 __device__ __forceinline__ bf16x8 frag(const uint8_t* lds, int base, int kk, int lane) {
-  if constexpr (SRC == KC) return frag_kc(lds, base, kk, lane);
+  if constexpr (SRC == KC) return frag_kc<BK>(lds, base, kk, lane);
   else return frag_mc<C>(lds, base, kk, lane);
 }
 
 // --------------------------------------------------------------------------
 // The kernel
 // --------------------------------------------------------------------------
-template <int ASRC, int BSRC, int EPI, int MODE>
-__global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(Args a) {
-  constexpr int A_BYTES = BM * BK * 2;  // 16 KB
-  constexpr int B_BYTES = BN * BK * 2;  // 32 KB
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+template <class Cfg, int ASRC, int BSRC, int EPI, int MODE>
+__global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NW = Cfg::NW, STAGES = Cfg::STAGES;
+  constexpr int WM = Cfg::WM, WN = Cfg::WN, WTM = Cfg::WTM, WTN = Cfg::WTN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   // ---- tile decode ---------------------------------------------------
-  const int nblocks = gridDim.x;
-  const int L = xcd_remap(blockIdx.x, nblocks);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
   int e, mt, nt;
-  if constexpr (MODE == MGROUP) {
-    const int per_group = GROUP_M * a.n_ntiles;
-    const int grp = L / per_group, within = L % per_group;
-    const int gm = min(GROUP_M, a.n_mtiles - grp * GROUP_M);
-    mt = grp * GROUP_M + within % gm;
-    nt = within / gm;
-    e = a.tile_expert ? a.tile_expert[mt] : 0;
-    if (e < 0) return;
-  } else {
-    const int per_e = a.n_mtiles * a.n_ntiles;
-    e = L / per_e;
-    const int rem = L % per_e;
+  {
+    const int per_e = (MODE == KGROUP) ? a.n_mtiles * a.n_ntiles : 0x7fffffff;
+    e = (MODE == KGROUP) ? L / per_e : 0;
+    const int rem = (MODE == KGROUP) ? L % per_e : L;
     const int per_group = GROUP_M * a.n_ntiles;
     const int grp = rem / per_group, within = rem % per_group;
     const int gm = min(GROUP_M, a.n_mtiles - grp * GROUP_M);
     mt = grp * GROUP_M + within % gm;
     nt = within / gm;
+  }
+  if constexpr (MODE == MGROUP) {
+    if (a.tile_expert == nullptr) {
+      e = 0;
+    } else if (MOE_EXPERT_MAJOR) {
+      // tiles of expert e occupy [n_ntiles * mstart_e, n_ntiles * mend_e) in
+      // the logical order, m-tile fastest, so the m-tiles sharing one weight
+      // slice are adjacent and an expert's rows stay hot across its n-tiles
+      const int mq = L / a.n_ntiles;  // some m-tile inside the same expert's range
+      e = a.tile_expert[mq];
+      if (e < 0) return;
+      const int mstart = a.offsets[e] / BM;
+      const int me = (a.offsets[e + 1] - a.offsets[e]) / BM;
+      const int local = L - a.n_ntiles * mstart;
+      mt = mstart + local % me;
+      nt = local / me;
+    } else {
+      e = a.tile_expert[mt];
+      if (e < 0) return;
+    }
   }
 
   // row range of the segment (MGROUP: rows of the tile; KGROUP: the K range)
@@ -201,158 +299,175 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(Args a) {
 
   const uint16_t* Bg = a.B + (int64_t)e * a.strideB;
   const int64_t m0 = (MODE == MGROUP) ? (int64_t)mt * BM : 0;
-  const int mloc0 = (MODE == MGROUP) ? 0 : mt * BM;    // KGROUP: first output row (M dim)
+  const int mloc0 = (MODE == MGROUP) ? 0 : mt * BM;            // KGROUP: first output row (M dim)
   const int n0 = nt * (EPI == EPI_SWIGLU_FWD ? BN / 2 : BN);  // SWIGLU_FWD: f offset
 
   int nk;
-  int64_t k_base;  // first K index (KGROUP: first segment row)
+  if constexpr (MODE == MGROUP) nk = (a.K + BK - 1) / BK;
+  else nk = (int)((seg_hi - seg_lo + BK - 1) / BK);
+
+  // ---- buffer resources and per-lane load offsets ----------------------
+  __amdgpu_buffer_rsrc_t rA, rB;
+  KcLoad<BM, BK, NW> la_kc;
+  McLoad<BM, BK, NW> la_mc;
+  KcLoad<BN, BK, NW> lb_kc;
+  McLoad<BN, BK, NW> lb_mc;
   if constexpr (MODE == MGROUP) {
-    nk = (a.K + BK - 1) / BK;
-    k_base = 0;
-  } else {
-    nk = (int)((seg_hi - seg_lo + BK - 1) / BK);
-    k_base = seg_lo;
+    const int rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+    rA = make_rsrc(a.A + m0 * a.lda, (uint32_t)rows_valid * a.lda * 2);
+    la_kc.init([&](int r) -> uint32_t { return r < rows_valid ? (uint32_t)r * a.lda * 2 : kOOB; },
+               wave, lane);
+    if constexpr (BSRC == KC) {
+      rB = make_rsrc(Bg, (uint32_t)a.N * a.ldb * 2);
+      lb_kc.init([&](int r) -> uint32_t {
+        int n;
+        if constexpr (EPI == EPI_SWIGLU_FWD) {
+          const int f = n0 + (r & (BN / 2 - 1));
+          if (f >= a.F) return kOOB;
+          n = (r < BN / 2) ? f : a.F + f;
+        } else {
+          n = n0 + r;
+          if (n >= a.N) return kOOB;
+        }
+        return (uint32_t)n * a.ldb * 2;
+      }, wave, lane);
+    } else {  // B = W [K][N], N-contig
+      rB = make_rsrc(Bg, (uint32_t)a.K * a.ldb * 2);
+      lb_mc.init([&](int c) -> uint32_t { return n0 + c < a.N ? (uint32_t)(n0 + c) * 2 : kOOB; },
+                 wave, lane);
+    }
+  } else {  // KGROUP: A and B are rows of the segment, both M/N-contig
+    const uint32_t nrows = (uint32_t)(seg_hi - seg_lo);
+    rA = make_rsrc(a.A + seg_lo * a.lda, nrows * a.lda * 2);
+    rB = make_rsrc(a.B + seg_lo * a.ldb, nrows * a.ldb * 2);
+    la_mc.init([&](int c) -> uint32_t { return mloc0 + c < a.M ? (uint32_t)(mloc0 + c) * 2 : kOOB; },
+               wave, lane);
+    lb_mc.init([&](int c) -> uint32_t { return n0 + c < a.N ? (uint32_t)(n0 + c) * 2 : kOOB; },
+               wave, lane);
   }
 
-  // ---- operand row/col pointer functions ------------------------------
-  auto a_row_kc = [&](int r) -> const uint16_t* {   // A K-contig (MGROUP)
-    int64_t row = m0 + r;
-    return row < seg_hi ? a.A + row * a.lda : nullptr;
-  };
-  auto b_row_kc = [&](int r) -> const uint16_t* {   // B K-contig: B row n
-    int n;
-    if constexpr (EPI == EPI_SWIGLU_FWD) {
-      int f = n0 + (r & (BN / 2 - 1));
-      if (f >= a.F) return nullptr;
-      n = (r < BN / 2) ? f : a.F + f;
-    } else {
-      n = n0 + r;
-      if (n >= a.N) return nullptr;
-    }
-    return Bg + (int64_t)n * a.ldb;
-  };
+  constexpr int A_PER = (ASRC == KC) ? KcLoad<BM, BK, NW>::PER : McLoad<BM, BK, NW>::PER;
+  constexpr int B_PER = (BSRC == KC) ? KcLoad<BN, BK, NW>::PER : McLoad<BN, BK, NW>::PER;
+  constexpr int LOADS = A_PER + B_PER;  // DMA loads per wave per stage
 
-  KcStage<BM> sa_kc;
-  McStage<BM> sa_mc;
-  KcStage<BN> sb_kc;
-  McStage<BN> sb_mc;
-
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BK;
-    if constexpr (ASRC == KC) {
-      sa_kc.load(a_row_kc, k0, a.K, tid);
-    } else {  // A MN-contig: k-rows are segment rows (KGROUP)
-      auto krow = [&](int kr) -> const uint16_t* {
-        int64_t row = k_base + k0 + kr;
-        return row < seg_hi ? a.A + row * a.lda + mloc0 : nullptr;
-      };
-      sa_mc.load(krow, mloc0, a.M, tid);
-    }
-    if constexpr (BSRC == KC) {
-      sb_kc.load(b_row_kc, k0, a.K, tid);
+  // load i of stage kt: i < A_PER is an A region, the rest B regions
+  auto issue_one = [&](int kt, int i) {
+    uint8_t* As = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
+    uint8_t* Bs = As + Cfg::A_BYTES;
+    const int nrows = (int)(seg_hi - seg_lo);
+    if (i < A_PER) {
+      if constexpr (ASRC == KC) {
+        la_kc.issue(rA, As, wave, i, kt, a.K);
+      } else {
+        la_mc.issue(rA, As, wave, i, kt, [&](int k) -> uint32_t {
+          return k < nrows ? (uint32_t)k * a.lda * 2 : kOOB;
+        });
+      }
     } else {
-      if constexpr (MODE == MGROUP) {  // B = W [K][N] N-contig
-        auto krow = [&](int kr) -> const uint16_t* {
-          int k = k0 + kr;
-          return k < a.K ? Bg + (int64_t)k * a.ldb + n0 : nullptr;
-        };
-        sb_mc.load(krow, n0, a.N, tid);
-      } else {  // B = rows of the segment, N-contig
-        auto krow = [&](int kr) -> const uint16_t* {
-          int64_t row = k_base + k0 + kr;
-          return row < seg_hi ? a.B + row * a.ldb + n0 : nullptr;
-        };
-        sb_mc.load(krow, n0, a.N, tid);
+      const int j = i - A_PER;
+      if constexpr (BSRC == KC) {
+        lb_kc.issue(rB, Bs, wave, j, kt, a.K);
+      } else if constexpr (MODE == MGROUP) {
+        lb_mc.issue(rB, Bs, wave, j, kt, [&](int k) -> uint32_t {
+          return k < a.K ? (uint32_t)k * a.ldb * 2 : kOOB;
+        });
+      } else {
+        lb_mc.issue(rB, Bs, wave, j, kt, [&](int k) -> uint32_t {
+          return k < nrows ? (uint32_t)k * a.ldb * 2 : kOOB;
+        });
       }
     }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* As = smem + buf * (A_BYTES + B_BYTES);
-    uint8_t* Bs = As + A_BYTES;
-    if constexpr (ASRC == KC) sa_kc.store(As, tid); else sa_mc.store(As, tid);
-    if constexpr (BSRC == KC) sb_kc.store(Bs, tid); else sb_mc.store(Bs, tid);
   };
 
   // wave's fragment bases
-  const int a_base0 = wm * 64;  // rows of A tile
-  int b_base[4];
+  int a_base[WM], b_base[WN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (EPI == EPI_SWIGLU_FWD)
-      b_base[j] = (j < 2) ? (wn * 64 + j * 32) : (BN / 2 + wn * 64 + (j - 2) * 32);
+  for (int i = 0; i < WM; ++i) a_base[i] = wm * WTM + 32 * i;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    if constexpr (EPI == EPI_SWIGLU_FWD)  // first half gate columns, second half the matching up
+      b_base[j] = (j < WN / 2) ? (wn * (WTN / 2) + 32 * j)
+                               : (BN / 2 + wn * (WTN / 2) + 32 * (j - WN / 2));
     else
-      b_base[j] = wn * 128 + j * 32;
+      b_base[j] = wn * WTN + 32 * j;
   }
 
-  f32x16 acc[2][4];
+  f32x16 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load_tile(kt + 1);
-      const uint8_t* As = smem + cur * (A_BYTES + B_BYTES);
-      const uint8_t* Bs = As + A_BYTES;
+  // prologue: stages 0 .. STAGES-2 in flight
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 af[2], bfr[4];
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = frag<ASRC, BM>(As, a_base0 + i * 32, kk, lane);
+      for (int i = 0; i < LOADS; ++i) issue_one(s, i);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once only the stages issued after it are in flight
+    const int ahead = min(STAGES - 2, nk - 1 - kt);
+    wait_stages<LOADS, STAGES - 2>(ahead);
+    // every wave's part of stage kt is in LDS, and every wave has finished
+    // reading the buffer that stage kt+STAGES-1 overwrites
+    __builtin_amdgcn_s_barrier();
+    const int nxt = kt + STAGES - 1;
+    const uint8_t* As = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
+    const uint8_t* Bs = As + Cfg::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = frag<BSRC, BN>(Bs, b_base[j], kk, lane);
+    for (int kk = 0; kk < Cfg::KK; ++kk) {
+      bf16x8 af[WM], bfr[WN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WM; ++i) af[i] = frag<ASRC, BM, BK>(As, a_base[i], kk, lane);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WN; ++j) bfr[j] = frag<BSRC, BN, BK>(Bs, b_base[j], kk, lane);
+      // this stage's share of the next DMA loads, spread over the k-steps
+      if (nxt < nk) {
+#pragma unroll
+        for (int i = kk * LOADS / Cfg::KK; i < (kk + 1) * LOADS / Cfg::KK; ++i) issue_one(nxt, i);
       }
-      if (kt + 1 < nk) store_tile(cur ^ 1);
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 
   // ---- epilogue --------------------------------------------------------
-  // acc[i][j][r]: row m = a_base0 + 32 i + (lane & 31)
+  // acc[i][j][r]: row m = a_base[i] + (lane & 31)
   //               col n = b_base[j] + 8 (r/4) + 4 (lane/32) + r%4
   const int mrow = lane & 31;
   const int csub = 4 * (lane >> 5);
   if constexpr (EPI == EPI_SWIGLU_FWD) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = m0 + a_base0 + 32 * i + mrow;
+    for (int i = 0; i < WM; ++i) {
+      const int64_t row = m0 + a_base[i] + mrow;
       if (row >= seg_hi) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < WN / 2; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = n0 + wn * 64 + j * 32 + 8 * g + csub;
+          const int f = n0 + b_base[j] + 8 * g + csub;
           if (f >= a.F) continue;
+          const f32x16& G = acc[i][j];
+          const f32x16& U = acc[i][j + WN / 2];
           float hv[4];
-          uint32_t gw[2], uw[2], hw[2];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float gt = acc[i][j][4 * g + q], up = acc[i][j + 2][4 * g + q];
+            const float gt = G[4 * g + q], up = U[4 * g + q];
             hv[q] = gt / (1.0f + expf(-gt)) * up;
           }
-          hw[0] = pack_bf16x2(hv[0], hv[1]);
-          hw[1] = pack_bf16x2(hv[2], hv[3]);
-          *(u32x2*)(a.C + row * a.ldc + f) = u32x2{hw[0], hw[1]};
+          *(u32x2*)(a.C + row * a.ldc + f) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
           if (a.C2) {
-            gw[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-            gw[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-            uw[0] = pack_bf16x2(acc[i][j + 2][4 * g + 0], acc[i][j + 2][4 * g + 1]);
-            uw[1] = pack_bf16x2(acc[i][j + 2][4 * g + 2], acc[i][j + 2][4 * g + 3]);
             uint16_t* ar = a.C2 + row * (int64_t)(2 * a.F);
-            *(u32x2*)(ar + f) = u32x2{gw[0], gw[1]};
-            *(u32x2*)(ar + a.F + f) = u32x2{uw[0], uw[1]};
+            *(u32x2*)(ar + f) = u32x2{pack_bf16x2(G[4 * g + 0], G[4 * g + 1]),
+                                     pack_bf16x2(G[4 * g + 2], G[4 * g + 3])};
+            *(u32x2*)(ar + a.F + f) = u32x2{pack_bf16x2(U[4 * g + 0], U[4 * g + 1]),
+                                            pack_bf16x2(U[4 * g + 2], U[4 * g + 3])};
           }
         }
       }
@@ -360,26 +475,26 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(Args a) {
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
     // acc = dh[row][f]; aux = act [rows][2F]; C = dact [rows][2F]
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = m0 + a_base0 + 32 * i + mrow;
+    for (int i = 0; i < WM; ++i) {
+      const int64_t row = m0 + a_base[i] + mrow;
       if (row >= seg_hi) continue;
       const uint16_t* actr = a.aux + row * (int64_t)(2 * a.F);
       uint16_t* dactr = a.C + row * (int64_t)(2 * a.F);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int f = n0 + b_base[j] + 8 * g + csub;
           if (f >= a.F) continue;
-          u32x2 gw = *(const u32x2*)(actr + f);
-          u32x2 uw = *(const u32x2*)(actr + a.F + f);
-          float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
-          float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
+          const u32x2 gw = *(const u32x2*)(actr + f);
+          const u32x2 uw = *(const u32x2*)(actr + a.F + f);
+          const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
+          const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
           float dg[4], du[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float dh = acc[i][j][4 * g + q];
-            float sg = 1.0f / (1.0f + expf(-gt[q]));
+            const float dh = acc[i][j][4 * g + q];
+            const float sg = 1.0f / (1.0f + expf(-gt[q]));
             dg[q] = dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg)));
             du[q] = dh * gt[q] * sg;
           }
@@ -392,11 +507,11 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(Args a) {
     uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
     const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = (MODE == MGROUP ? m0 : (int64_t)mloc0) + a_base0 + 32 * i + mrow;
+    for (int i = 0; i < WM; ++i) {
+      const int64_t row = (MODE == MGROUP ? m0 : (int64_t)mloc0) + a_base[i] + mrow;
       if (row >= rows_lim) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = n0 + b_base[j] + 8 * g + csub;
@@ -410,19 +525,32 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(Args a) {
   }
 }
 
-template <int ASRC, int BSRC, int EPI, int MODE>
+template <class Cfg, int ASRC, int BSRC, int EPI, int MODE>
 static hipError_t launch(const Args& a, int nblocks, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<ASRC, BSRC, EPI, MODE>), dim3(nblocks), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<Cfg, ASRC, BSRC, EPI, MODE>), dim3(nblocks), dim3(Cfg::NT),
+                     0, s, a);
   return hipGetLastError();
+}
+
+// M-grouped launch: routed segments use the 128-row tile (= alignment), the
+// dense single group (shared experts) the 256-row tile
+template <int ASRC, int BSRC, int EPI>
+static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_tile_wide, int ncols,
+                              hipStream_t s) {
+  if (a.tile_expert) {
+    a.n_mtiles = (int)((a.m_rows + CfgRows::BM - 1) / CfgRows::BM);
+    a.n_ntiles = (ncols + n_cols_per_tile_rows - 1) / n_cols_per_tile_rows;
+    return launch<CfgRows, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  }
+  a.n_mtiles = (int)((a.m_rows + CfgWide::BM - 1) / CfgWide::BM);
+  a.n_ntiles = (ncols + n_cols_per_tile_wide - 1) / n_cols_per_tile_wide;
+  return launch<CfgWide, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
 }
 
 }  // namespace gemm
 
 using namespace gemm;
-
-// M-tiles covering m_rows rows
-static inline int mtiles(int64_t m_rows) { return (int)((m_rows + BM - 1) / BM); }
 
 hipError_t launch_gemm_gate_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
                                const int32_t* counts, const int32_t* tile_expert,
@@ -432,9 +560,9 @@ hipError_t launch_gemm_gate_up(int G, int64_t m_rows, int H, int F, const int32_
   a.A = x_rows; a.B = w1; a.C = h; a.C2 = act;
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = 2 * F; a.K = H; a.F = F;
-  a.lda = H; a.ldb = H; a.ldc = F; a.strideB = (int64_t)2 * F * H;
-  a.n_mtiles = mtiles(m_rows); a.n_ntiles = (F + BN / 2 - 1) / (BN / 2); a.G = G;
-  return launch<KC, KC, EPI_SWIGLU_FWD, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  a.lda = H; a.ldb = H; a.ldc = F; a.strideB = (int64_t)2 * F * H; a.G = G;
+  // an n-tile covers BN/2 gate columns and the matching BN/2 up columns
+  return launch_rows<KC, KC, EPI_SWIGLU_FWD>(a, CfgRows::BN / 2, CfgWide::BN / 2, F, s);
 }
 
 hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
@@ -445,9 +573,8 @@ hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* 
   a.A = h; a.B = w2; a.C = y_rows;
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = F; a.F = F;
-  a.lda = F; a.ldb = F; a.ldc = H; a.strideB = (int64_t)H * F;
-  a.n_mtiles = mtiles(m_rows); a.n_ntiles = (H + BN - 1) / BN; a.G = G;
-  return launch<KC, KC, EPI_STORE, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  a.lda = F; a.ldb = F; a.ldc = H; a.strideB = (int64_t)H * F; a.G = G;
+  return launch_rows<KC, KC, EPI_STORE>(a, CfgRows::BN, CfgWide::BN, H, s);
 }
 
 hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
@@ -458,9 +585,8 @@ hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int
   a.A = dy_rows; a.B = w2; a.C = dact; a.aux = act;
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = F; a.K = H; a.F = F;
-  a.lda = H; a.ldb = F; a.ldc = 2 * F; a.strideB = (int64_t)H * F;
-  a.n_mtiles = mtiles(m_rows); a.n_ntiles = (F + BN - 1) / BN; a.G = G;
-  return launch<KC, MC, EPI_SWIGLU_BWD, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  a.lda = H; a.ldb = F; a.ldc = 2 * F; a.strideB = (int64_t)H * F; a.G = G;
+  return launch_rows<KC, MC, EPI_SWIGLU_BWD>(a, CfgRows::BN, CfgWide::BN, F, s);
 }
 
 hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
@@ -471,9 +597,8 @@ hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.A = dact; a.B = w1; a.C = dx_rows;
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = 2 * F; a.F = F;
-  a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = (int64_t)2 * F * H;
-  a.n_mtiles = mtiles(m_rows); a.n_ntiles = (H + BN - 1) / BN; a.G = G;
-  return launch<KC, MC, EPI_STORE, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = (int64_t)2 * F * H; a.G = G;
+  return launch_rows<KC, MC, EPI_STORE>(a, CfgRows::BN, CfgWide::BN, H, s);
 }
 
 // dW2[g] [H,F] = dy_rows_g^T [H, rows] . h_g [rows, F]
@@ -485,8 +610,9 @@ hipError_t launch_gemm_wgrad_down(int G, int64_t m_rows, int H, int F, const int
   a.offsets = offsets; a.counts = counts;
   a.m_rows = m_rows; a.M = H; a.N = F; a.F = F;
   a.lda = H; a.ldb = F; a.ldc = F; a.strideB = 0; a.strideC = (int64_t)H * F;
-  a.n_mtiles = (H + BM - 1) / BM; a.n_ntiles = (F + BN - 1) / BN; a.G = G;
-  return launch<MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  a.n_mtiles = (H + CfgWide::BM - 1) / CfgWide::BM; a.n_ntiles = (F + CfgWide::BN - 1) / CfgWide::BN;
+  a.G = G;
+  return launch<CfgWide, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
 }
 
 // dW1[g] [2F,H] = dact_g^T [2F, rows] . x_rows_g [rows, H]
@@ -498,8 +624,9 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.offsets = offsets; a.counts = counts;
   a.m_rows = m_rows; a.M = 2 * F; a.N = H; a.F = F;
   a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = 0; a.strideC = (int64_t)2 * F * H;
-  a.n_mtiles = (2 * F + BM - 1) / BM; a.n_ntiles = (H + BN - 1) / BN; a.G = G;
-  return launch<MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  a.n_mtiles = (2 * F + CfgWide::BM - 1) / CfgWide::BM; a.n_ntiles = (H + CfgWide::BN - 1) / CfgWide::BN;
+  a.G = G;
+  return launch<CfgWide, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
 }
 
 }  // namespace moe
