@@ -73,8 +73,14 @@ struct TileCfg {
 #ifndef MOE_EXPERT_MAJOR
 #define MOE_EXPERT_MAJOR 1
 #endif
-using CfgRows = TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, 2, 4>;  // 128-row expert segments
-using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4>;  // weight grads, dense expert
+#ifndef MOE_ROWS_WGN
+#define MOE_ROWS_WGN 4
+#endif
+#ifndef MOE_WIDE_WGN
+#define MOE_WIDE_WGN 4
+#endif
+using CfgRows = TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, 2, MOE_ROWS_WGN>;  // 128-row segments
+using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, MOE_WIDE_WGN>;  // wgrad, dense
 static_assert(CfgRows::LDS_BYTES <= 160 * 1024 && CfgWide::LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
 
@@ -254,7 +260,14 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
   const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   // ---- tile decode ---------------------------------------------------
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // Live tile count: for routed segments only the tiles below offsets[G] hold
+  // rows; the grid is sized for the capacity bound.  Spreading the live tiles
+  // (not the grid) over the XCDs keeps every XCD busy; the surplus ids exit.
+  int n_mt = a.n_mtiles;
+  if (MODE == MGROUP && a.tile_expert != nullptr) n_mt = a.offsets[a.G] / BM;
+  const int ntiles_live = (MODE == MGROUP) ? n_mt * a.n_ntiles : (int)gridDim.x;
+  if ((int)blockIdx.x >= ntiles_live) return;
+  const int L = xcd_remap(blockIdx.x, ntiles_live);
   int e, mt, nt;
   {
     const int per_e = (MODE == KGROUP) ? a.n_mtiles * a.n_ntiles : 0x7fffffff;
@@ -262,7 +275,7 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
     const int rem = (MODE == KGROUP) ? L % per_e : L;
     const int per_group = GROUP_M * a.n_ntiles;
     const int grp = rem / per_group, within = rem % per_group;
-    const int gm = min(GROUP_M, a.n_mtiles - grp * GROUP_M);
+    const int gm = min(GROUP_M, n_mt - grp * GROUP_M);
     mt = grp * GROUP_M + within % gm;
     nt = within / gm;
   }
@@ -437,90 +450,136 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
     }
   }
 
-  // ---- epilogue --------------------------------------------------------
-  // acc[i][j][r]: row m = a_base[i] + (lane & 31)
-  //               col n = b_base[j] + 8 (r/4) + 4 (lane/32) + r%4
+  // ---- epilogue: through LDS, coalesced 16-byte row stores ---------------
+  // acc[i][j][r] holds row m = a_base[i] + (lane & 31) and column
+  // n = b_base[j] + 8 (r/4) + 4 (lane/32) + r%4 of the tile.  Each output plane
+  // (a BM x PC slice of one output tensor) is written to LDS as bf16 from the
+  // registers, then copied out row by row with every lane moving 16 bytes, so a
+  // wave's store covers whole cache lines.  The operand ring is free once all
+  // waves pass the first barrier (the last stage was waited for in full).
   const int mrow = lane & 31;
   const int csub = 4 * (lane >> 5);
+  constexpr int PC_FULL = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;  // plane columns
+  constexpr int PITCH_FULL = PC_FULL * 2 + 16;
+  constexpr int PC = (BM * PITCH_FULL <= Cfg::LDS_BYTES) ? PC_FULL : PC_FULL / 2;
+  constexpr int PITCH = PC * 2 + 16;  // 16-byte pad: row starts rotate over the banks
+  constexpr int NPART = PC_FULL / PC;
+  static_assert(BM * PITCH <= Cfg::LDS_BYTES, "output plane must fit the operand ring");
+  uint8_t* plane = smem;
+
+  // column of block j, group g relative to the plane (gate/up blocks map to the
+  // same plane column)
+  auto pcol = [&](int j, int g) -> int {
+    const int c = b_base[j] + 8 * g + csub;
+    return (EPI == EPI_SWIGLU_FWD && j >= WN / 2) ? c - BN / 2 : c;
+  };
+  auto put4 = [&](int m, int c, float v0, float v1, float v2, float v3) {
+    *(u32x2*)(plane + m * PITCH + c * 2) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+  };
+  // plane (columns [part*PC, part*PC + PC) of the tile) -> global rows
+  auto store_plane = [&](uint16_t* gbase, int64_t ld, int64_t row0, int64_t row_lim, int col0,
+                         int col_lim) {
+    __syncthreads();
+    constexpr int CPR = PC / 8;
+    for (int q = tid; q < BM * CPR; q += Cfg::NT) {
+      const int r = q / CPR, c = q % CPR;
+      const int64_t row = row0 + r;
+      const int col = col0 + c * 8;
+      if (row < row_lim && col < col_lim)
+        *(u32x4*)(gbase + row * ld + col) = *(const u32x4*)(plane + r * PITCH + c * 16);
+    }
+  };
+  __syncthreads();
+
   if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // planes: h, then act's gate half, then act's up half
+    const int nplanes = a.C2 ? 3 : 1;
+    for (int pl = 0; pl < nplanes; ++pl) {
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int64_t row = m0 + a_base[i] + mrow;
-      if (row >= seg_hi) continue;
+      for (int part = 0; part < NPART; ++part) {
+        if (pl + part > 0) __syncthreads();
 #pragma unroll
-      for (int j = 0; j < WN / 2; ++j) {
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = n0 + b_base[j] + 8 * g + csub;
-          if (f >= a.F) continue;
-          const f32x16& G = acc[i][j];
-          const f32x16& U = acc[i][j + WN / 2];
-          float hv[4];
+          for (int j = 0; j < WN / 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gt = G[4 * g + q], up = U[4 * g + q];
-            hv[q] = gt / (1.0f + expf(-gt)) * up;
-          }
-          *(u32x2*)(a.C + row * a.ldc + f) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-          if (a.C2) {
-            uint16_t* ar = a.C2 + row * (int64_t)(2 * a.F);
-            *(u32x2*)(ar + f) = u32x2{pack_bf16x2(G[4 * g + 0], G[4 * g + 1]),
-                                     pack_bf16x2(G[4 * g + 2], G[4 * g + 3])};
-            *(u32x2*)(ar + a.F + f) = u32x2{pack_bf16x2(U[4 * g + 0], U[4 * g + 1]),
-                                            pack_bf16x2(U[4 * g + 2], U[4 * g + 3])};
-          }
-        }
+            for (int g = 0; g < 4; ++g) {
+              const int c = pcol(j, g) - part * PC;
+              if (c < 0 || c >= PC) continue;
+              const f32x16& G = acc[i][j];
+              const f32x16& U = acc[i][j + WN / 2];
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float gt = G[4 * g + q], up = U[4 * g + q];
+                v[q] = pl == 0 ? gt / (1.0f + expf(-gt)) * up : (pl == 1 ? gt : up);
+              }
+              put4(a_base[i] + mrow, c, v[0], v[1], v[2], v[3]);
+            }
+        if (pl == 0)
+          store_plane(a.C, a.ldc, m0, seg_hi, n0 + part * PC, a.F);
+        else
+          store_plane(a.C2 + (pl == 2 ? a.F : 0), 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // acc = dh[row][f]; aux = act [rows][2F]; C = dact [rows][2F]
+    // acc = dh[row][f]; act = [gate | up] rows of the forward; two planes:
+    // dgate (into dact's first half) and dup (second half)
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int64_t row = m0 + a_base[i] + mrow;
-      if (row >= seg_hi) continue;
-      const uint16_t* actr = a.aux + row * (int64_t)(2 * a.F);
-      uint16_t* dactr = a.C + row * (int64_t)(2 * a.F);
+    for (int pl = 0; pl < 2; ++pl) {
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
+      for (int part = 0; part < NPART; ++part) {
+        if (pl + part > 0) __syncthreads();
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = n0 + b_base[j] + 8 * g + csub;
-          if (f >= a.F) continue;
-          const u32x2 gw = *(const u32x2*)(actr + f);
-          const u32x2 uw = *(const u32x2*)(actr + a.F + f);
-          const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
-          const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
-          float dg[4], du[4];
+        for (int i = 0; i < WM; ++i) {
+          const int64_t row = m0 + a_base[i] + mrow;
+          const bool rin = row < seg_hi;
+          const uint16_t* actr = a.aux + (rin ? row : 0) * (int64_t)(2 * a.F);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dh = acc[i][j][4 * g + q];
-            const float sg = 1.0f / (1.0f + expf(-gt[q]));
-            dg[q] = dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg)));
-            du[q] = dh * gt[q] * sg;
-          }
-          *(u32x2*)(dactr + f) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          *(u32x2*)(dactr + a.F + f) = u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int c = pcol(j, g) - part * PC;
+              if (c < 0 || c >= PC) continue;
+              const int f = n0 + b_base[j] + 8 * g + csub;
+              float v[4] = {0.f, 0.f, 0.f, 0.f};
+              if (rin && f < a.F) {
+                const u32x2 gw = *(const u32x2*)(actr + f);
+                const u32x2 uw = *(const u32x2*)(actr + a.F + f);
+                const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
+                const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const float dh = acc[i][j][4 * g + q];
+                  const float sg = 1.0f / (1.0f + expf(-gt[q]));
+                  v[q] = pl == 0 ? dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg))) : dh * gt[q] * sg;
+                }
+              }
+              put4(a_base[i] + mrow, c, v[0], v[1], v[2], v[3]);
+            }
         }
+        store_plane(a.C + (pl == 1 ? a.F : 0), 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);
       }
     }
   } else {  // EPI_STORE
     uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
+    const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
     const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const int64_t row = (MODE == MGROUP ? m0 : (int64_t)mloc0) + a_base[i] + mrow;
-      if (row >= rows_lim) continue;
+    for (int part = 0; part < NPART; ++part) {
+      if (part > 0) __syncthreads();
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + b_base[j] + 8 * g + csub;
-          if (n >= a.N) continue;
-          *(u32x2*)(Cg + row * a.ldc + n) =
-              u32x2{pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
-                    pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-        }
-      }
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = pcol(j, g) - part * PC;
+            if (c < 0 || c >= PC) continue;
+            put4(a_base[i] + mrow, c, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                 acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          }
+      store_plane(Cg, a.ldc, row0, rows_lim, n0 + part * PC, a.N);
     }
   }
 }
