@@ -225,26 +225,85 @@ __device__ __forceinline__ bf16x8 frag_kc(const uint8_t* lds, int base, int kk, 
   return *(const bf16x8*)(lds + row * (BK * 2) + ((c ^ kc_swz<BK>(row)) << 4));
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// LDS address of the first of the two transposing reads that build lane l's
+// fragment of an MN-contig tile; the second read is 4 k-rows (8*C bytes) on.
 template <int C>
-__device__ __forceinline__ bf16x8 frag_mc(const uint8_t* lds, int base, int kk, int lane) {
+__device__ __forceinline__ uint32_t mc_addr(const uint8_t* lds, int base, int kk, int lane) {
   const int g = lane >> 4, li = lane & 15;
   const int col = base + 16 * (g & 1) + 4 * (li & 3);
-  const int kb = 16 * kk + 8 * (g >> 1) + (li >> 2);
+  const int k0 = 16 * kk + 8 * (g >> 1) + (li >> 2);
   const int c = col >> 3, sub = (col & 7) * 2;
-  const int k0 = kb, k1 = kb + 4;
-  const uint8_t* p0 = lds + k0 * (C * 2) + ((c ^ (4 * (k0 & 3))) << 4) + sub;
-  const uint8_t* p1 = lds + k1 * (C * 2) + ((c ^ (4 * (k1 & 3))) << 4) + sub;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p0));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p1));
+  return lds_addr(lds) + k0 * (C * 2) + ((c ^ (4 * (k0 & 3))) << 4) + sub;
+}
+
+__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int SRC, int C, int BK>
-__device__ __forceinline__ bf16x8 frag(const uint8_t* lds, int base, int kk, int lane) {
-  if constexpr (SRC == KC) return frag_kc<BK>(lds, base, kk, lane);
-  else return frag_mc<C>(lds, base, kk, lane);
+// Fragments of an MN-contig tile via ds_read_b64_tr_b16, issued from inline
+// asm together with their own s_waitcnt lgkmcnt(0): the outputs are complete
+// when the block ends.  Written this way because the compiler treats the
+// transposing-read builtin as possibly aliasing the in-flight LDS-DMA stores
+// and would otherwise wait for every outstanding operand load before it.
+template <int C>
+__device__ __forceinline__ void mc_frags2(uint32_t a0, uint32_t a1, bf16x8& f0, bf16x8& f1) {
+  s16x4 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "i"(8 * C));
+  f0 = join(r0, r1);
+  f1 = join(r2, r3);
+}
+template <int C>
+__device__ __forceinline__ void mc_frags4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          bf16x8& f0, bf16x8& f1, bf16x8& f2, bf16x8& f3) {
+  s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(8 * C));
+  f0 = join(r0, r1);
+  f1 = join(r2, r3);
+  f2 = join(r4, r5);
+  f3 = join(r6, r7);
+}
+
+// all NF fragments of one operand for k-step kk
+template <int SRC, int NF, int C, int BK>
+__device__ __forceinline__ void load_frags(const uint8_t* lds, const int* base, int kk, int lane,
+                                           bf16x8* f) {
+  if constexpr (SRC == KC) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) f[i] = frag_kc<BK>(lds, base[i], kk, lane);
+  } else {
+    static_assert(NF == 2 || NF == 4, "fragment count");
+    if constexpr (NF == 2) {
+      mc_frags2<C>(mc_addr<C>(lds, base[0], kk, lane), mc_addr<C>(lds, base[1], kk, lane), f[0], f[1]);
+    } else {
+      mc_frags4<C>(mc_addr<C>(lds, base[0], kk, lane), mc_addr<C>(lds, base[1], kk, lane),
+                   mc_addr<C>(lds, base[2], kk, lane), mc_addr<C>(lds, base[3], kk, lane), f[0],
+                   f[1], f[2], f[3]);
+    }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -433,10 +492,8 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
 #pragma unroll
     for (int kk = 0; kk < Cfg::KK; ++kk) {
       bf16x8 af[WM], bfr[WN];
-#pragma unroll
-      for (int i = 0; i < WM; ++i) af[i] = frag<ASRC, BM, BK>(As, a_base[i], kk, lane);
-#pragma unroll
-      for (int j = 0; j < WN; ++j) bfr[j] = frag<BSRC, BN, BK>(Bs, b_base[j], kk, lane);
+      load_frags<ASRC, WM, BM, BK>(As, a_base, kk, lane, af);
+      load_frags<BSRC, WN, BN, BK>(Bs, b_base, kk, lane, bfr);
       // this stage's share of the next DMA loads, spread over the k-steps
       if (nxt < nk) {
 #pragma unroll
