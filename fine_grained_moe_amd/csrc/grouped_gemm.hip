@@ -580,44 +580,61 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // acc = dh[row][f]; act = [gate | up] rows of the forward; two planes:
-    // dgate (into dact's first half) and dup (second half)
-#pragma unroll
-    for (int pl = 0; pl < 2; ++pl) {
-#pragma unroll
-      for (int part = 0; part < NPART; ++part) {
-        if (pl + part > 0) __syncthreads();
-#pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const int64_t row = m0 + a_base[i] + mrow;
-          const bool rin = row < seg_hi;
-          const uint16_t* actr = a.aux + (rin ? row : 0) * (int64_t)(2 * a.F);
-#pragma unroll
-          for (int j = 0; j < WN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int c = pcol(j, g) - part * PC;
-              if (c < 0 || c >= PC) continue;
-              const int f = n0 + b_base[j] + 8 * g + csub;
-              float v[4] = {0.f, 0.f, 0.f, 0.f};
-              if (rin && f < a.F) {
-                const u32x2 gw = *(const u32x2*)(actr + f);
-                const u32x2 uw = *(const u32x2*)(actr + a.F + f);
-                const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
-                const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  const float dh = acc[i][j][4 * g + q];
-                  const float sg = 1.0f / (1.0f + expf(-gt[q]));
-                  v[q] = pl == 0 ? dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg))) : dh * gt[q] * sg;
-                }
-              }
-              put4(a_base[i] + mrow, c, v[0], v[1], v[2], v[3]);
-            }
-        }
-        store_plane(a.C + (pl == 1 ? a.F : 0), 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);
+    // acc = dh[row][f].  The forward's act rows ([gate | up], bf16) for this
+    // tile are first copied into LDS with coalesced 16-byte loads (gate plane,
+    // then up plane).  Each lane reads its own gate/up values from LDS, turns
+    // dh into dgate in place, and writes dup over its own gate slots (each slot
+    // has exactly one reader), so the gate plane becomes the dup plane; both
+    // results then leave through the plane path into dact's two halves.
+    static_assert(NPART == 1, "SwiGLU backward runs on tiles whose act planes fit LDS");
+    static_assert(2 * BM * PITCH <= Cfg::LDS_BYTES, "gate and up planes must fit the ring");
+    uint8_t* gplane = smem;
+    uint8_t* uplane = smem + BM * PITCH;
+    {
+      constexpr int CPR = PC / 8;
+      for (int q = tid; q < 2 * BM * CPR; q += Cfg::NT) {
+        const int half = q / (BM * CPR), rq = q % (BM * CPR);
+        const int r = rq / CPR, c = rq % CPR;
+        const int64_t row = m0 + r;
+        const int f = n0 + c * 8;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (row < seg_hi && f < a.F) v = *(const u32x4*)(a.aux + row * (int64_t)(2 * a.F) + half * a.F + f);
+        *(u32x4*)((half ? uplane : gplane) + r * PITCH + c * 16) = v;
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = a_base[i] + mrow, c = pcol(j, g);
+          const u32x2 gw = *(const u32x2*)(gplane + m * PITCH + c * 2);
+          const u32x2 uw = *(const u32x2*)(uplane + m * PITCH + c * 2);
+          const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
+          const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
+          float du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dh = acc[i][j][4 * g + q];
+            const float sg = 1.0f / (1.0f + expf(-gt[q]));
+            acc[i][j][4 * g + q] = dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg)));
+            du[q] = dh * gt[q] * sg;
+          }
+          put4(m, c, du[0], du[1], du[2], du[3]);  // plane == gplane
+        }
+    store_plane(a.C + a.F, 2 * (int64_t)a.F, m0, seg_hi, n0, a.F);  // dup half
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          put4(a_base[i] + mrow, pcol(j, g), acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+               acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    store_plane(a.C, 2 * (int64_t)a.F, m0, seg_hi, n0, a.F);  // dgate half
   } else {  // EPI_STORE
     uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
     const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
@@ -654,14 +671,22 @@ static hipError_t launch(const Args& a, int nblocks, hipStream_t s) {
 template <int ASRC, int BSRC, int EPI>
 static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_tile_wide, int ncols,
                               hipStream_t s) {
-  if (a.tile_expert) {
+  // routed segments need the 128-row tile (= alignment); the SwiGLU-backward
+  // epilogue stages two act planes in LDS, which only the 128-row tile leaves
+  // room for; everything else dense takes the 256-row tile
+  auto rows = [&]() {
     a.n_mtiles = (int)((a.m_rows + CfgRows::BM - 1) / CfgRows::BM);
     a.n_ntiles = (ncols + n_cols_per_tile_rows - 1) / n_cols_per_tile_rows;
     return launch<CfgRows, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+  };
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    return rows();
+  } else {
+    if (a.tile_expert) return rows();
+    a.n_mtiles = (int)((a.m_rows + CfgWide::BM - 1) / CfgWide::BM);
+    a.n_ntiles = (ncols + n_cols_per_tile_wide - 1) / n_cols_per_tile_wide;
+    return launch<CfgWide, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
   }
-  a.n_mtiles = (int)((a.m_rows + CfgWide::BM - 1) / CfgWide::BM);
-  a.n_ntiles = (ncols + n_cols_per_tile_wide - 1) / n_cols_per_tile_wide;
-  return launch<CfgWide, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
 }
 
 }  // namespace gemm
