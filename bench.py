@@ -24,6 +24,36 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0
 
 
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch) on this workload, scaled by the counters' reading for a plain 1 GiB
+# device copy (FETCH_SIZE reads half the bytes a copy moves: factor 2.0;
+# WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
+# source they were taken on, identified by its SHA-256; otherwise reported null.
+COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+TRAFFIC_SOURCE_SHA256 = "2996fcdfc604aba6669d38037423b15cf8575f7788938ec60eb5e0bbcef74a74"
+TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
+    "gate_up_fwd": (3127821.4, 405504.0), "down_fwd": (1179243.9, 491520.0),
+    "shared_gate_up_fwd": (348301.3, 135168.0), "shared_down_fwd": (180309.3, 81920.0),
+    "down_dgrad": (1504996.3, 270336.0), "gate_up_dgrad": (2420786.0, 491520.0),
+    "down_wgrad": (624304.0, 1802240.0), "gate_up_wgrad": (1124915.3, 3604480.0),
+    "shared_down_dgrad": (352415.5, 90112.0), "shared_gate_up_dgrad": (360540.8, 81920.0),
+    "shared_down_wgrad": (217183.4, 28160.0), "shared_gate_up_wgrad": (434272.2, 56320.0),
+}
+
+
+def traffic_of(name, w):
+    import hashlib
+    src = os.path.join(ROOT, "fine_grained_moe_amd", "csrc", "grouped_gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if w.name != "fwdbwd" or sha != TRAFFIC_SOURCE_SHA256 or name not in TRAFFIC_KIB:
+        return {"traffic": None}
+    fk, wk = TRAFFIC_KIB[name]
+    gb = (fk * COUNTER_FACTORS["FETCH_SIZE"] + wk * COUNTER_FACTORS["WRITE_SIZE"]) * 1024 / 1e9
+    return {"traffic": round(gb, 3), "traffic_unit": "GB per launch",
+            "traffic_read_gb": round(fk * COUNTER_FACTORS["FETCH_SIZE"] * 1024 / 1e9, 3),
+            "traffic_write_gb": round(wk * COUNTER_FACTORS["WRITE_SIZE"] * 1024 / 1e9, 3)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -33,6 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the same batch the CPU oracle runs on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device to device (known HBM bytes, for scaling "
+                         "hardware byte counters)")
     return ap.parse_args()
 
 
@@ -70,43 +103,96 @@ class Layer:
             dx=e(T, H))
         self.ev = None
 
+    # the twelve grouped-GEMM launches of one step, in launch order
+    GEMMS = ("gate_up_fwd", "down_fwd", "shared_gate_up_fwd", "shared_down_fwd",
+             "down_dgrad", "gate_up_dgrad", "down_wgrad", "gate_up_wgrad",
+             "shared_down_dgrad", "shared_gate_up_dgrad", "shared_down_wgrad",
+             "shared_gate_up_wgrad")
+
+    def _gemm(self, name, ev, fn):
+        """Launch one grouped GEMM, bracketed by events when ev is a dict."""
+        if ev is not None:
+            ev[name][0].record()
+        fn()
+        if ev is not None:
+            ev[name][1].record()
+
     def forward(self, ev=None):
         M, g, b, K = self.M, self.g, self.b, self.K
         p = b["perm"]
+        seg = (p["offsets"], p["counts"], p["tile_expert"])
         M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"])
         M.moe_permute(b["topk_idx"], g["x"], self.E, out=p, ws=b["perm_ws"])
-        if ev is not None:
-            ev[0].record()
-        M.moe_grouped_gate_up_fwd(p["x_rows"], g["w1"], p["offsets"], p["counts"], p["tile_expert"],
-                                  act=b["act"], h=b["h"])
-        if ev is not None:
-            ev[1].record()
-        M.moe_grouped_down_fwd(b["h"], g["w2"], p["offsets"], p["counts"], p["tile_expert"],
-                               y_rows=b["y_rows"])
-        M.moe_grouped_swiglu_fwd(g["x"], self.w1f, self.w2f, act=b["act_sh"], h=b["h_sh"],
-                                 y_rows=b["y_sh"])
-        if ev is not None:
-            ev[2].record()
+        self._gemm("gate_up_fwd", ev, lambda: M.moe_grouped_gate_up_fwd(
+            p["x_rows"], g["w1"], *seg, act=b["act"], h=b["h"]))
+        self._gemm("down_fwd", ev, lambda: M.moe_grouped_down_fwd(
+            b["h"], g["w2"], *seg, y_rows=b["y_rows"]))
+        self._gemm("shared_gate_up_fwd", ev, lambda: M.moe_grouped_gate_up_fwd(
+            g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"]))
+        self._gemm("shared_down_fwd", ev, lambda: M.moe_grouped_down_fwd(
+            b["h_sh"], self.w2f, y_rows=b["y_sh"]))
         M.moe_combine(b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"])
 
     def backward(self, ev=None):
         M, g, b = self.M, self.g, self.b
         p = b["perm"]
+        seg = (p["offsets"], p["counts"], p["tile_expert"])
+        E = self.E
         M.moe_combine_bwd(g["dy"], b["y_rows"], p["row_of"], b["topk_w"], dy_rows=b["dy_rows"], dg=b["dg"])
-        if ev is not None:
-            ev[3].record()
-        M.moe_grouped_swiglu_bwd(p["x_rows"], g["w1"], g["w2"], b["act"], b["h"], b["dy_rows"],
-                                 p["offsets"], p["counts"], p["tile_expert"], dact=b["dact"],
-                                 dx_rows=b["dx_rows"], dw1=b["dw1"], dw2=b["dw2"])
-        M.moe_grouped_swiglu_bwd(g["x"], self.w1f, self.w2f, b["act_sh"], b["h_sh"], g["dy"],
-                                 dact=b["dact_sh"], dx_rows=b["dx_sh"], dw1=b["dw1_sh"],
-                                 dw2=b["dw2_sh"])
-        if ev is not None:
-            ev[4].record()
+        # routed experts: the four steps of moe_grouped_swiglu_bwd, one launch each
+        self._gemm("down_dgrad", ev, lambda: M.moe_grouped_down_dgrad(
+            g["w2"], b["act"], b["dy_rows"], *seg, dact=b["dact"]))
+        self._gemm("gate_up_dgrad", ev, lambda: M.moe_grouped_gate_up_dgrad(
+            g["w1"], b["dact"], *seg, dx_rows=b["dx_rows"]))
+        self._gemm("down_wgrad", ev, lambda: M.moe_grouped_down_wgrad(
+            b["dy_rows"], b["h"], E, *seg, dw2=b["dw2"]))
+        self._gemm("gate_up_wgrad", ev, lambda: M.moe_grouped_gate_up_wgrad(
+            b["dact"], p["x_rows"], E, *seg, dw1=b["dw1"]))
+        # shared experts: one dense group of width S*F
+        self._gemm("shared_down_dgrad", ev, lambda: M.moe_grouped_down_dgrad(
+            self.w2f, b["act_sh"], g["dy"], dact=b["dact_sh"]))
+        self._gemm("shared_gate_up_dgrad", ev, lambda: M.moe_grouped_gate_up_dgrad(
+            self.w1f, b["dact_sh"], dx_rows=b["dx_sh"]))
+        self._gemm("shared_down_wgrad", ev, lambda: M.moe_grouped_down_wgrad(
+            g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"]))
+        self._gemm("shared_gate_up_wgrad", ev, lambda: M.moe_grouped_gate_up_wgrad(
+            b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"]))
         M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
                         p["offsets"], p["counts"], dw_router=b["dw_router"],
                         dx_router=b["dx_router"], ws=b["rb_ws"])
         M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+
+
+def gemm_launch_flops(w, name):
+    """Useful (padding-free) flops of one grouped-GEMM launch: 2*rows*N*K with
+    rows = T*K routed rows, or T for the shared experts (one group of width S*F)."""
+    shared = name.startswith("shared_")
+    rows = w.T if shared else w.T * w.K
+    F = w.S * w.F if shared else w.F
+    mult = 2 if "gate_up" in name else 1      # gate/up GEMMs have 2F columns (or K = 2F)
+    return 2.0 * rows * w.H * F * mult
+
+
+def gemm_launch_bytes(w, name):
+    """Algorithmic HBM bytes of one launch: every operand read once and every
+    result written once, bf16, padding rows excluded."""
+    shared = name.startswith("shared_")
+    rows = w.T if shared else w.T * w.K
+    G = 1 if shared else w.E
+    F = w.S * w.F if shared else w.F
+    H = w.H
+    wt = 2 * G * 2 * F * H if "gate_up" in name else 2 * G * H * F      # one weight tensor
+    if name.endswith("gate_up_fwd"):
+        return rows * H * 2 + wt + rows * 3 * F * 2          # x rows; act (2F) + h (F)
+    if name.endswith("down_fwd"):
+        return rows * F * 2 + wt + rows * H * 2              # h; y rows
+    if name.endswith("down_dgrad"):
+        return rows * H * 2 + wt + rows * 2 * F * 2 * 2      # dy rows; act in, dact out
+    if name.endswith("gate_up_dgrad"):
+        return rows * 2 * F * 2 + wt + rows * H * 2          # dact; dx rows
+    if name.endswith("down_wgrad"):
+        return rows * H * 2 + rows * F * 2 + wt              # dy rows, h; dW2
+    return rows * 2 * F * 2 + rows * H * 2 + wt              # dact, x rows; dW1
 
 
 class LazyExperts:
@@ -164,6 +250,13 @@ def main():
     g = generate_torch(w, dev, with_dy=True)
     layer = Layer(M, g, w.K)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        # one plain copy kernel reading and writing exactly 2^30 bytes each
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         layer.forward(ev)
@@ -174,9 +267,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; events inside bracket the grouped GEMMs
-    n_ev = 5
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    # timed region: K whole steps; events inside bracket every grouped-GEMM launch
+    names = Layer.GEMMS if backward else Layer.GEMMS[:4]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names} for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -186,9 +280,8 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    gate_up_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    gemm_fwd_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
-    gemm_bwd_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if backward else 0.0
+    launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    gemm_ms = sum(launch_ms.values())
 
     # forward alone, timed the same way
     torch.cuda.synchronize()
@@ -205,11 +298,13 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     fwd_tflops = useful_flops(w, False) / (fwd_ms * 1e-3) / 1e12
     gemm_flops = gemm_useful_flops(w, backward)
-    gemm_ms = gemm_fwd_ms + gemm_bwd_ms
-    # the gate/up GEMM of the routed experts: useful flops T*K*2H*2F per launch
-    gate_up_flops = float(w.T) * w.K * 2 * w.H * 2 * w.F
-    achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+    # the dominant kernel: the grouped-GEMM launch with the longest average time
+    dom = max(names, key=lambda n: launch_ms[n])
+    achieved = gemm_launch_flops(w, dom) / (launch_ms[dom] * 1e-3) / 1e12
     counts = layer.b["perm"]["counts"].cpu().numpy()
+    launches = {n: {"ms": round(launch_ms[n], 4),
+                    "tflops": round(gemm_launch_flops(w, n) / (launch_ms[n] * 1e-3) / 1e12, 1),
+                    "algorithmic_gb": round(gemm_launch_bytes(w, n) / 1e9, 3)} for n in names}
 
     out = {
         "metric": "MoE layer useful TFLOP/s at T=8192 (fwd, fwd+bwd); % of bf16 MFMA peak",
@@ -235,10 +330,13 @@ def main():
         "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gemm_ms": round(gemm_ms, 4),
         "routed_nonempty_experts": int((counts > 0).sum()),
-        "roofline": {"kernel": "grouped_gemm gate/up + SwiGLU (routed experts)",
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": f"grouped GEMM {dom}", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "launch_ms": round(gate_up_ms, 4), "traffic": None},
+                     "launch_ms": round(launch_ms[dom], 4),
+                     "algorithmic_gb": round(gemm_launch_bytes(w, dom) / 1e9, 3),
+                     **traffic_of(dom, w)},
+        "gemm_launches": launches,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens)

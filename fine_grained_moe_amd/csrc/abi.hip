@@ -223,6 +223,57 @@ moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_
   return hip_status(e, __func__);
 }
 
+moe_status_t moe_grouped_down_dgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* w2,
+                                    const uint16_t* act, const uint16_t* dy_rows,
+                                    uint16_t* dact, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(w2 && act && dy_rows && dact, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_dgrad_down(G, m_rows, H, F, offsets, counts, tile_expert,
+                                                dy_rows, w2, act, dact, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_grouped_down_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* dy_rows,
+                                    const uint16_t* h, uint16_t* dw2, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  REQUIRE(dy_rows && h && dw2, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_wgrad_down(G, m_rows, H, F, offsets, counts, dy_rows, h, dw2,
+                                                (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_grouped_gate_up_dgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                       const int32_t* offsets, const int32_t* counts,
+                                       const int32_t* tile_expert, const uint16_t* w1,
+                                       const uint16_t* dact, uint16_t* dx_rows, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(w1 && dact && dx_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_dgrad_up(G, m_rows, H, F, offsets, counts, tile_expert, dact,
+                                              w1, dx_rows, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                       const int32_t* offsets, const int32_t* counts,
+                                       const int32_t* tile_expert, const uint16_t* dact,
+                                       const uint16_t* x_rows, uint16_t* dw1, void* stream) {
+  moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  REQUIRE(dact && x_rows && dw1, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_gemm_wgrad_up(G, m_rows, H, F, offsets, counts, dact, x_rows, dw1,
+                                              (hipStream_t)stream),
+                    __func__);
+}
+
 moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x_rows,
                            const float* w_router, const int32_t* topk_idx, const float* topk_s,
                            const float* dg, const int32_t* row_of, const int32_t* offsets,

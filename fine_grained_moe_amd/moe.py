@@ -40,6 +40,10 @@ _SIGS = {
     "moe_combine_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_swiglu_bwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
                                       _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_down_dgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_down_wgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_gate_up_dgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_grouped_gate_up_wgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_route_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                              _sz, _p]),
     "moe_permute_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
@@ -237,6 +241,57 @@ def moe_grouped_swiglu_bwd(x_rows, w1, w2, act, h, dy_rows, offsets=None, counts
                                        _ptr(dx_rows, BF16, "dx_rows"), _ptr(dw1, BF16, "dw1"),
                                        _ptr(dw2, BF16, "dw2"), _stream()))
     return dact, dx_rows, dw1, dw2
+
+
+def _seg(offsets, counts, tile_expert):
+    return _ptr(offsets, I32), _ptr(counts, I32), _ptr(tile_expert, I32)
+
+
+def moe_grouped_down_dgrad(w2, act, dy_rows, offsets=None, counts=None, tile_expert=None,
+                           dact=None):
+    """dact = SwiGLU-backward(dy_rows . w2[g], act).  Returns dact."""
+    M, H = dy_rows.shape
+    G, _, F = w2.shape
+    dact = torch.empty((M, 2 * F), dtype=BF16, device=dy_rows.device) if dact is None else dact
+    _check(_lib.moe_grouped_down_dgrad(G, M, H, F, *_seg(offsets, counts, tile_expert),
+                                       _ptr(w2, BF16, "w2"), _ptr(act, BF16, "act"),
+                                       _ptr(dy_rows, BF16, "dy_rows"), _ptr(dact, BF16, "dact"),
+                                       _stream()))
+    return dact
+
+
+def moe_grouped_down_wgrad(dy_rows, h, G, offsets=None, counts=None, tile_expert=None, dw2=None):
+    """dw2[g] = dy_rows_g^T . h_g.  Returns dw2 [G,H,F]."""
+    M, H = dy_rows.shape
+    F = h.shape[1]
+    dw2 = torch.empty((G, H, F), dtype=BF16, device=h.device) if dw2 is None else dw2
+    _check(_lib.moe_grouped_down_wgrad(G, M, H, F, *_seg(offsets, counts, tile_expert),
+                                       _ptr(dy_rows, BF16, "dy_rows"), _ptr(h, BF16, "h"),
+                                       _ptr(dw2, BF16, "dw2"), _stream()))
+    return dw2
+
+
+def moe_grouped_gate_up_dgrad(w1, dact, offsets=None, counts=None, tile_expert=None, dx_rows=None):
+    """dx_rows = dact . w1[g].  Returns dx_rows."""
+    M, twoF = dact.shape
+    G, _, H = w1.shape
+    dx_rows = torch.empty((M, H), dtype=BF16, device=dact.device) if dx_rows is None else dx_rows
+    _check(_lib.moe_grouped_gate_up_dgrad(G, M, H, twoF // 2, *_seg(offsets, counts, tile_expert),
+                                          _ptr(w1, BF16, "w1"), _ptr(dact, BF16, "dact"),
+                                          _ptr(dx_rows, BF16, "dx_rows"), _stream()))
+    return dx_rows
+
+
+def moe_grouped_gate_up_wgrad(dact, x_rows, G, offsets=None, counts=None, tile_expert=None,
+                              dw1=None):
+    """dw1[g] = dact_g^T . x_rows_g.  Returns dw1 [G,2F,H]."""
+    M, twoF = dact.shape
+    H = x_rows.shape[1]
+    dw1 = torch.empty((G, twoF, H), dtype=BF16, device=dact.device) if dw1 is None else dw1
+    _check(_lib.moe_grouped_gate_up_wgrad(G, M, H, twoF // 2, *_seg(offsets, counts, tile_expert),
+                                          _ptr(dact, BF16, "dact"), _ptr(x_rows, BF16, "x_rows"),
+                                          _ptr(dw1, BF16, "dw1"), _stream()))
+    return dw1
 
 
 def moe_route_bwd(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, counts,

@@ -213,6 +213,38 @@ moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_
                                     void* stream);
 
 /*
+ * The four steps of moe_grouped_swiglu_bwd as entry points of their own, same
+ * argument meanings; moe_grouped_swiglu_bwd is exactly
+ * down_dgrad, gate_up_dgrad, down_wgrad, gate_up_wgrad in that order.  The
+ * data gradients and the weight gradients do not depend on each other once
+ * dact exists, so a caller may run the weight-gradient steps on another stream.
+ *   moe_grouped_down_dgrad    : dact  = SwiGLU-backward(dy_rows . w2[g], act)
+ *   moe_grouped_down_wgrad    : dw2[g] = dy_rows_g^T . h_g      (zero for an empty group)
+ *   moe_grouped_gate_up_dgrad : dx_rows = dact . w1[g]
+ *   moe_grouped_gate_up_wgrad : dw1[g] = dact_g^T . x_rows_g    (zero for an empty group)
+ * tile_expert is only validated by the weight-gradient steps.  m_rows == 0 is
+ * a no-op for the data-gradient steps; the weight-gradient steps still write
+ * zeros.
+ */
+moe_status_t moe_grouped_down_dgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* w2,
+                                    const uint16_t* act, const uint16_t* dy_rows,
+                                    uint16_t* dact, void* stream);
+moe_status_t moe_grouped_down_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* tile_expert, const uint16_t* dy_rows,
+                                    const uint16_t* h, uint16_t* dw2, void* stream);
+moe_status_t moe_grouped_gate_up_dgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                       const int32_t* offsets, const int32_t* counts,
+                                       const int32_t* tile_expert, const uint16_t* w1,
+                                       const uint16_t* dact, uint16_t* dx_rows, void* stream);
+moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_t F,
+                                       const int32_t* offsets, const int32_t* counts,
+                                       const int32_t* tile_expert, const uint16_t* dact,
+                                       const uint16_t* x_rows, uint16_t* dw1, void* stream);
+
+/*
  * moe_route_bwd - backward of moe_route's weights through the selected scores
  * (routing decision held fixed, no bias gradient):
  *   S_t        = sum_j topk_s[t,j],  g = topk_s / S_t

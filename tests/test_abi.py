@@ -130,3 +130,18 @@ def test_route_bwd_rejects(lib):
     f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]
     assert f(16, 64, 8, 2, *[_p(FAKE)] * 11, 16, _p(None)) == 3
     assert f(16, 64, 8, 2, _p(None), *[_p(FAKE)] * 10, 1 << 30, _p(None)) == 1
+
+
+def test_backward_steps_reject(lib):
+    # (name, number of operand pointers after the three segment pointers)
+    for name, nptr in (("moe_grouped_down_dgrad", 4), ("moe_grouped_down_wgrad", 3),
+                       ("moe_grouped_gate_up_dgrad", 3), ("moe_grouped_gate_up_wgrad", 3)):
+        f = getattr(lib, name)
+        f.argtypes = ([ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] +
+                      [ctypes.c_void_p] * (3 + nptr + 1))
+        seg = [_p(FAKE)] * 3
+        ops = [_p(FAKE)] * nptr
+        assert f(4, 256, 64, 48, *seg, *ops, _p(None)) == 2, name            # F % 32
+        assert f(4, 200, 64, 32, *seg, *ops, _p(None)) == 1, name            # rows % 128
+        assert f(2, 256, 64, 32, _p(None), _p(None), _p(None), *ops, _p(None)) == 1, name
+        assert f(4, 256, 64, 32, *seg, _p(None), *ops[1:], _p(None)) == 1, name  # null operand

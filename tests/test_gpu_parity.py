@@ -223,6 +223,40 @@ def test_deterministic(M):
         assert torch.equal(a, b)
 
 
+def test_backward_steps_match_composite(M):
+    """The four backward step entry points, called one by one (weight
+    gradients on a second stream), reproduce moe_grouped_swiglu_bwd bit for bit,
+    routed (grouped) and shared (dense)."""
+    w = MID["T1000_H512_E16_K4_F352"]
+    inp = generate_numpy(w, with_dy=True)
+    g = to_gpu(inp)
+    y, ctx, grads = run_layer(M, g, w.K, True)
+    p = ctx["perm"]
+    E = g["w1"].shape[0]
+    seg = (p["offsets"], p["counts"], p["tile_expert"])
+    side = torch.cuda.Stream()
+    dact = M.moe_grouped_down_dgrad(g["w2"], ctx["act"], grads["dy_rows"], *seg)
+    side.wait_stream(torch.cuda.current_stream())
+    dx_rows = M.moe_grouped_gate_up_dgrad(g["w1"], dact, *seg)
+    with torch.cuda.stream(side):
+        dw2 = M.moe_grouped_down_wgrad(grads["dy_rows"], ctx["h"], E, *seg)
+        dw1 = M.moe_grouped_gate_up_wgrad(dact, p["x_rows"], E, *seg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    valid = p["src_token"] >= 0
+    assert torch.equal(dact[valid], grads["dact"][valid])
+    assert torch.equal(dx_rows[valid], grads["dx_rows"][valid])
+    assert torch.equal(dw1, grads["dw1"]) and torch.equal(dw2, grads["dw2"])
+    # shared experts: one dense group
+    dact_sh = M.moe_grouped_down_dgrad(ctx["w2_shf"], ctx["act_sh"], g["dy"])
+    dx_sh = M.moe_grouped_gate_up_dgrad(ctx["w1_shf"], dact_sh)
+    dw2_sh = M.moe_grouped_down_wgrad(g["dy"], ctx["h_sh"], 1)
+    dw1_sh = M.moe_grouped_gate_up_wgrad(dact_sh, g["x"], 1)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_sh, grads["dx_shared"])
+    assert torch.equal(dw1_sh, grads["dw1_sh"]) and torch.equal(dw2_sh, grads["dw2_sh"])
+
+
 def test_empty_batch(M):
     E, K, H, F = 8, 2, 64, 32
     x = torch.zeros((0, H), dtype=torch.bfloat16, device=DEV)
