@@ -37,15 +37,18 @@
 // accumulator of block (i,j) holds C[m][n] with m = l%32 (one row per lane)
 // and n = 8*(r/4) + 4*(l/32) + r%4 (four consecutive columns per group of
 // four registers): epilogues store 4 bf16 (8 bytes) per lane per group.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace gemm {
 
-template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_>
+template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MINB_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WGM = WGM_, WGN = WGN_;
+  static constexpr int MINB = MINB_;                    // workgroups resident per CU
   static constexpr int NW = WGM * WGN, NT = NW * 64;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   static constexpr int WM = WTM / 32, WN = WTN / 32;    // 32x32 MFMA blocks per wave
@@ -53,6 +56,8 @@ struct TileCfg {
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(KK % 2 == 0, "fragment double buffering pairs k-steps");
+  static_assert(LDS_BYTES * MINB <= 160 * 1024, "LDS per CU");
 };
 // Tile depth and pipeline depth are build-time tunables (defaults measured best).
 #ifndef MOE_ROWS_BK
@@ -73,18 +78,35 @@ struct TileCfg {
 #ifndef MOE_EXPERT_MAJOR
 #define MOE_EXPERT_MAJOR 1
 #endif
+#ifndef MOE_ROWS_WGM
+#define MOE_ROWS_WGM 2
+#endif
 #ifndef MOE_ROWS_WGN
 #define MOE_ROWS_WGN 4
 #endif
-#ifndef MOE_WIDE_WGN
-#define MOE_WIDE_WGN 4
+#ifndef MOE_ROWS_MINB
+#define MOE_ROWS_MINB 1
 #endif
-using CfgRows = TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, 2, MOE_ROWS_WGN>;  // 128-row segments
-using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, MOE_WIDE_WGN>;  // wgrad, dense
-static_assert(CfgRows::LDS_BYTES <= 160 * 1024 && CfgWide::LDS_BYTES <= 160 * 1024, "LDS");
+// 128 x 256 row tiles; default 8 waves (wave tile 64 x 64), one workgroup per CU,
+// 64-deep k stages (128-byte row segments per load)
+using CfgRows =
+    TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, MOE_ROWS_WGM, MOE_ROWS_WGN, MOE_ROWS_MINB>;
+// 256 x 256 tiles of 8 waves (wave tile 128 x 64), one workgroup per CU
+using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4, 1>;
+// tile of the K-grouped weight-gradient products: 0 = CfgWide, 1 = CfgRows
+#ifndef MOE_WGRAD_ROWS
+#define MOE_WGRAD_ROWS 0
+#endif
+using CfgWgrad = std::conditional_t<MOE_WGRAD_ROWS != 0, CfgRows, CfgWide>;
 static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
 
-constexpr int GROUP_M = 4;  // m-tiles per rasterization group
+constexpr int GROUP_M = 4;  // m-tiles per rasterization group (row-grouped, non-expert-major)
+// K-grouped weight gradients: m-tiles per rasterization group inside one
+// expert (0 = all of them, so each column slab of the second operand is used
+// by every m-tile while it is resident in L2)
+#ifndef MOE_KGROUP_GM
+#define MOE_KGROUP_GM 4
+#endif
 
 enum Src { KC = 0, MC = 1 };
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2 };
@@ -121,14 +143,35 @@ struct Args {
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           (int)kRsrcWord3);
+// raw buffer resource: base, stride 0, num_records = bytes.  The arguments
+// are workgroup-uniform; readfirstlane makes that explicit so the descriptor
+// lives in SGPRs, as the buffer instruction requires.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3};
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
+// One wave-level global -> LDS load of 64 x 16 B.  lds: wave-uniform LDS byte
+// address of the 1 KB destination.  Issued from inline asm so that the compiler
+// does not treat the LDS writes as aliasing every later LDS read (it would put
+// a wait for all outstanding loads before each transposing read); the kernel
+// orders them itself with explicit vmcnt waits and barriers.  M0 is used by
+// nothing else in these kernels.
+__device__ __forceinline__ void dma16(const u32x4& rs, uint32_t lds, uint32_t voff) {
+  lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 // s_waitcnt vmcnt(n) leaving expcnt/lgkmcnt unconstrained (gfx9 encoding)
@@ -136,6 +179,7 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
 }
 
 // wait until at most `ahead` stages of LOADS loads each are still in flight
@@ -147,6 +191,11 @@ __device__ __forceinline__ void wait_stages(int ahead) {
     if (ahead >= MAXA) wait_vmcnt<LOADS * MAXA>();
     else wait_stages<LOADS, MAXA - 1>(ahead);
   }
+}
+
+// every wave's LDS reads done, then a workgroup barrier that orders memory
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int BK>
@@ -175,8 +224,8 @@ struct KcLoad {
       kel[i] = c * 8;
     }
   }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int wave, int i,
-                                        int kt, int K) const {
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t lds, int wave, int i, int kt,
+                                        int K) const {
     const int q = i * NW + wave;
     const bool kin = kt * BK + kel[i] < K;
     const uint32_t v = (off[i] == kOOB || !kin) ? kOOB : off[i] + (uint32_t)kt * (BK * 2);
@@ -206,8 +255,8 @@ struct McLoad {
   }
   // krow_off(k) -> byte offset of global k-row k, or kOOB
   template <class KRowOff>
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int wave, int i,
-                                        int kt, KRowOff krow_off) const {
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t lds, int wave, int i, int kt,
+                                        KRowOff krow_off) const {
     const int q = i * NW + wave;
     const uint32_t ko = krow_off(kt * BK + kr[i]);
     const uint32_t v = (ko == kOOB || coff[i] == kOOB) ? kOOB : ko + coff[i];
@@ -225,10 +274,6 @@ __device__ __forceinline__ bf16x8 frag_kc(const uint8_t* lds, int base, int kk, 
   return *(const bf16x8*)(lds + row * (BK * 2) + ((c ^ kc_swz<BK>(row)) << 4));
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
-}
-
 // LDS address of the first of the two transposing reads that build lane l's
 // fragment of an MN-contig tile; the second read is 4 k-rows (8*C bytes) on.
 template <int C>
@@ -240,82 +285,49 @@ __device__ __forceinline__ uint32_t mc_addr(const uint8_t* lds, int base, int kk
   return lds_addr(lds) + k0 * (C * 2) + ((c ^ (4 * (k0 & 3))) << 4) + sub;
 }
 
-__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ s16x4 read_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(size_t)addr);
 }
 
-// Fragments of an MN-contig tile via ds_read_b64_tr_b16, issued from inline
-// asm together with their own s_waitcnt lgkmcnt(0): the outputs are complete
-// when the block ends.  Written this way because the compiler treats the
-// transposing-read builtin as possibly aliasing the in-flight LDS-DMA stores
-// and would otherwise wait for every outstanding operand load before it.
+// fragment of an MN-contig tile: two ds_read_b64_tr_b16 (gfx950 transposing
+// LDS read), four k-rows apart
 template <int C>
-__device__ __forceinline__ void mc_frags2(uint32_t a0, uint32_t a1, bf16x8& f0, bf16x8& f1) {
-  s16x4 r0, r1, r2, r3;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %2, %5\n\t"
-      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a0), "v"(a1), "i"(8 * C));
-  f0 = join(r0, r1);
-  f1 = join(r2, r3);
-}
-template <int C>
-__device__ __forceinline__ void mc_frags4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                          bf16x8& f0, bf16x8& f1, bf16x8& f2, bf16x8& f3) {
-  s16x4 r0, r1, r2, r3, r4, r5, r6, r7;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %2, %9\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %10\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %6, %11\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(8 * C));
-  f0 = join(r0, r1);
-  f1 = join(r2, r3);
-  f2 = join(r4, r5);
-  f3 = join(r6, r7);
+__device__ __forceinline__ bf16x8 frag_mc(const uint8_t* lds, int base, int kk, int lane) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const uint32_t a0 = mc_addr<C>(lds, base, kk, lane);
+  const s16x4 lo = read_tr16(a0), hi = read_tr16(a0 + 8 * C);
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // all NF fragments of one operand for k-step kk
 template <int SRC, int NF, int C, int BK>
 __device__ __forceinline__ void load_frags(const uint8_t* lds, const int* base, int kk, int lane,
                                            bf16x8* f) {
-  if constexpr (SRC == KC) {
 #pragma unroll
-    for (int i = 0; i < NF; ++i) f[i] = frag_kc<BK>(lds, base[i], kk, lane);
-  } else {
-    static_assert(NF == 2 || NF == 4, "fragment count");
-    if constexpr (NF == 2) {
-      mc_frags2<C>(mc_addr<C>(lds, base[0], kk, lane), mc_addr<C>(lds, base[1], kk, lane), f[0], f[1]);
-    } else {
-      mc_frags4<C>(mc_addr<C>(lds, base[0], kk, lane), mc_addr<C>(lds, base[1], kk, lane),
-                   mc_addr<C>(lds, base[2], kk, lane), mc_addr<C>(lds, base[3], kk, lane), f[0],
-                   f[1], f[2], f[3]);
-    }
-  }
+  for (int i = 0; i < NF; ++i)
+    f[i] = (SRC == KC) ? frag_kc<BK>(lds, base[i], kk, lane) : frag_mc<C>(lds, base[i], kk, lane);
+}
+
+// SwiGLU's logistic function in the GEMM epilogues: hardware exp2 and
+// reciprocal (about 1 ulp each).  The results are rounded to bf16 next, so the
+// correctly rounded library forms would only cost time.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
 }
 
 // --------------------------------------------------------------------------
 // The kernel
 // --------------------------------------------------------------------------
 template <class Cfg, int ASRC, int BSRC, int EPI, int MODE>
-__global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
+__global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NW = Cfg::NW, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, WTM = Cfg::WTM, WTN = Cfg::WTN;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   // ---- tile decode ---------------------------------------------------
@@ -332,10 +344,11 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
     const int per_e = (MODE == KGROUP) ? a.n_mtiles * a.n_ntiles : 0x7fffffff;
     e = (MODE == KGROUP) ? L / per_e : 0;
     const int rem = (MODE == KGROUP) ? L % per_e : L;
-    const int per_group = GROUP_M * a.n_ntiles;
+    const int GM = (MODE == KGROUP) ? (MOE_KGROUP_GM > 0 ? MOE_KGROUP_GM : n_mt) : GROUP_M;
+    const int per_group = GM * a.n_ntiles;
     const int grp = rem / per_group, within = rem % per_group;
-    const int gm = min(GROUP_M, n_mt - grp * GROUP_M);
-    mt = grp * GROUP_M + within % gm;
+    const int gm = min(GM, n_mt - grp * GM);
+    mt = grp * GM + within % gm;
     nt = within / gm;
   }
   if constexpr (MODE == MGROUP) {
@@ -379,7 +392,7 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
   else nk = (int)((seg_hi - seg_lo + BK - 1) / BK);
 
   // ---- buffer resources and per-lane load offsets ----------------------
-  __amdgpu_buffer_rsrc_t rA, rB;
+  u32x4 rA, rB;
   KcLoad<BM, BK, NW> la_kc;
   McLoad<BM, BK, NW> la_mc;
   KcLoad<BN, BK, NW> lb_kc;
@@ -423,9 +436,10 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
   constexpr int LOADS = A_PER + B_PER;  // DMA loads per wave per stage
 
   // load i of stage kt: i < A_PER is an A region, the rest B regions
+  const uint32_t smem_base = lds_addr(smem);
   auto issue_one = [&](int kt, int i) {
-    uint8_t* As = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
-    uint8_t* Bs = As + Cfg::A_BYTES;
+    const uint32_t As = smem_base + (kt % STAGES) * Cfg::STAGE_BYTES;
+    const uint32_t Bs = As + Cfg::A_BYTES;
     const int nrows = (int)(seg_hi - seg_lo);
     if (i < A_PER) {
       if constexpr (ASRC == KC) {
@@ -472,57 +486,109 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // prologue: stages 0 .. STAGES-2 in flight
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk)
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) issue_one(s, i);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once only the stages issued after it are in flight
-    const int ahead = min(STAGES - 2, nk - 1 - kt);
-    wait_stages<LOADS, STAGES - 2>(ahead);
-    // every wave's part of stage kt is in LDS, and every wave has finished
-    // reading the buffer that stage kt+STAGES-1 overwrites
-    __builtin_amdgcn_s_barrier();
-    const int nxt = kt + STAGES - 1;
+  // One k-step (16 deep) of the wave tile: WM x WN MFMAs on fragments that
+  // were read from LDS one k-step earlier (double-buffered registers), so the
+  // LDS latency of step s+1 hides behind the MFMAs of step s.
+  auto frags = [&](int kt, int kk, bf16x8* af, bf16x8* bfr) {
     const uint8_t* As = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
     const uint8_t* Bs = As + Cfg::A_BYTES;
+    load_frags<ASRC, WM, BM, BK>(As, a_base, kk, lane, af);
+    load_frags<BSRC, WN, BN, BK>(Bs, b_base, kk, lane, bfr);
+  };
+
+  // The pipeline runs without branches: loads of stages past the last one
+  // have k past K, so the hardware fills their LDS slots with zeros (nothing
+  // reads them), and every wait counts the same number of loads.
+  // prologue: stages 0 .. STAGES-2 in flight, stage 0 landed, its first
+  // fragments in registers
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) issue_one(s, i);
+  wait_vmcnt<LOADS * (STAGES - 2)>();
+  lds_barrier();
+  bf16x8 af[2][WM], bfr[2][WN];
+  frags(0, 0, af[0], bfr[0]);
+
+  // each k-step issues PER_KK of the LOADS loads of stage kt+STAGES-1, so
+  // when the last k-step of stage kt waits for stage kt+1, the loads issued
+  // after stage kt+1 are the full stages kt+2 .. kt+STAGES-2 and the first
+  // KK-1 shares of stage kt+STAGES-1
+  // With two stages the refill of stage kt+1 must be complete when stage kt
+  // ends, so its loads go out during the first KK-1 k-steps only.
+  constexpr int ISSUE_KK = (STAGES == 2) ? Cfg::KK - 1 : Cfg::KK;
+  constexpr int PER_KK = (LOADS + ISSUE_KK - 1) / ISSUE_KK;
+  constexpr int LATER =
+      (STAGES == 2) ? 0
+                    : LOADS * (STAGES - 3) +
+                          ((Cfg::KK - 1) * PER_KK < LOADS ? (Cfg::KK - 1) * PER_KK : LOADS);
+  static_assert(STAGES >= 2 && ISSUE_KK >= 1, "pipeline depth");
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt+STAGES-1 goes into the buffer stage kt-1 used; every wave
+    // finished reading that one before the barrier that preceded stage kt
+    const int nxt = kt + STAGES - 1;
 #pragma unroll
     for (int kk = 0; kk < Cfg::KK; ++kk) {
-      bf16x8 af[WM], bfr[WN];
-      load_frags<ASRC, WM, BM, BK>(As, a_base, kk, lane, af);
-      load_frags<BSRC, WN, BN, BK>(Bs, b_base, kk, lane, bfr);
-      // this stage's share of the next DMA loads, spread over the k-steps
-      if (nxt < nk) {
-#pragma unroll
-        for (int i = kk * LOADS / Cfg::KK; i < (kk + 1) * LOADS / Cfg::KK; ++i) issue_one(nxt, i);
+      const int cur = kk & 1, nb = cur ^ 1;
+      if (kk + 1 < Cfg::KK) {
+        frags(kt, kk + 1, af[nb], bfr[nb]);
+      } else {
+        // stage kt+1 has landed once only the loads issued after it remain
+        wait_vmcnt<LATER>();
+        lds_barrier();
+        frags(kt + 1, 0, af[nb], bfr[nb]);
       }
+      // keep the reads ahead of the MFMAs that hide their latency
+      __builtin_amdgcn_sched_barrier(0);
+      // this k-step's share of the next stage's DMA loads, between MFMAs
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < WN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+          const int t = i * WN + j;
+          const int li = kk * PER_KK + t;
+          if (t < PER_KK && li < LOADS) {
+            issue_one(nxt, li);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
     }
   }
+  wait_vmcnt<0>();
 
   // ---- epilogue: through LDS, coalesced 16-byte row stores ---------------
   // acc[i][j][r] holds row m = a_base[i] + (lane & 31) and column
   // n = b_base[j] + 8 (r/4) + 4 (lane/32) + r%4 of the tile.  Each output plane
   // (a BM x PC slice of one output tensor) is written to LDS as bf16 from the
   // registers, then copied out row by row with every lane moving 16 bytes, so a
-  // wave's store covers whole cache lines.  The operand ring is free once all
+  // wave's store covers whole cache lines.  Plane rows are unpadded; the 16-byte
+  // chunks of row m are XOR-swizzled by m, which spreads the column writes of
+  // the 32 rows a wave holds over the banks.  The operand ring is free once all
   // waves pass the first barrier (the last stage was waited for in full).
+  // Barriers here order LDS only: the global stores are left in flight (a
+  // workgroup fence would wait for each plane's stores before the next).
   const int mrow = lane & 31;
   const int csub = 4 * (lane >> 5);
   constexpr int PC_FULL = (EPI == EPI_SWIGLU_FWD) ? BN / 2 : BN;  // plane columns
-  constexpr int PITCH_FULL = PC_FULL * 2 + 16;
-  constexpr int PC = (BM * PITCH_FULL <= Cfg::LDS_BYTES) ? PC_FULL : PC_FULL / 2;
-  constexpr int PITCH = PC * 2 + 16;  // 16-byte pad: row starts rotate over the banks
+  // the SwiGLU backward keeps two planes (gate and up of the forward) in LDS
+  constexpr int NPL = (EPI == EPI_SWIGLU_BWD) ? 2 : 1;
+  constexpr int PC = (NPL * BM * PC_FULL * 2 <= Cfg::LDS_BYTES) ? PC_FULL : PC_FULL / 2;
+  constexpr int PITCH = PC * 2;
   constexpr int NPART = PC_FULL / PC;
-  static_assert(BM * PITCH <= Cfg::LDS_BYTES, "output plane must fit the operand ring");
+  constexpr int CPR = PC / 8;                        // 16-byte chunks per plane row
+  constexpr int SWZ = (CPR < 32 ? CPR : 32) - 1;     // chunk swizzle mask
+  static_assert((CPR & (CPR - 1)) == 0, "plane rows hold a power-of-two number of chunks");
+  static_assert(NPL * BM * PITCH <= Cfg::LDS_BYTES, "output planes must fit the operand ring");
+  static_assert((BM * CPR) % Cfg::NT == 0, "plane copy is a whole number of rounds");
+  // 16-byte copies in flight per thread in a plane copy (the SwiGLU backward
+  // holds its dgate accumulators across the copies: one at a time there)
+  constexpr int UNR_MAX = (EPI == EPI_SWIGLU_BWD) ? 1 : 4;
   uint8_t* plane = smem;
+  auto poff = [](int m, int c) -> int {  // byte offset of element (m, c) of a plane
+    return m * PITCH + ((((c >> 3) ^ (m & SWZ))) << 4) + ((c & 7) << 1);
+  };
 
   // column of block j, group g relative to the plane (gate/up blocks map to the
   // same plane column)
@@ -530,23 +596,36 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
     const int c = b_base[j] + 8 * g + csub;
     return (EPI == EPI_SWIGLU_FWD && j >= WN / 2) ? c - BN / 2 : c;
   };
-  auto put4 = [&](int m, int c, float v0, float v1, float v2, float v3) {
-    *(u32x2*)(plane + m * PITCH + c * 2) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+  auto in_part = [&](int c) -> bool { return NPART == 1 || (c >= 0 && c < PC); };
+  auto put4 = [&](uint8_t* pl, int m, int c, float v0, float v1, float v2, float v3) {
+    *(u32x2*)(pl + poff(m, c)) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
   };
-  // plane (columns [part*PC, part*PC + PC) of the tile) -> global rows
-  auto store_plane = [&](uint16_t* gbase, int64_t ld, int64_t row0, int64_t row_lim, int col0,
-                         int col_lim) {
-    __syncthreads();
-    constexpr int CPR = PC / 8;
-    for (int q = tid; q < BM * CPR; q += Cfg::NT) {
-      const int r = q / CPR, c = q % CPR;
-      const int64_t row = row0 + r;
-      const int col = col0 + c * 8;
-      if (row < row_lim && col < col_lim)
-        *(u32x4*)(gbase + row * ld + col) = *(const u32x4*)(plane + r * PITCH + c * 16);
+  // plane (columns [part*PC, part*PC + PC) of the tile) -> global rows: every
+  // round's LDS reads are issued before its stores
+  auto store_plane = [&](const uint8_t* pl, uint16_t* gbase, int64_t ld, int64_t row0,
+                         int64_t row_lim, int col0, int col_lim) {
+    lds_barrier();
+    constexpr int ROUNDS = BM * CPR / Cfg::NT;
+    constexpr int UNR = ROUNDS < UNR_MAX ? ROUNDS : UNR_MAX;
+    static_assert(ROUNDS % UNR == 0, "plane copy batches");
+#pragma unroll 1  // batches stay sequential: bounded registers
+    for (int u0 = 0; u0 < ROUNDS; u0 += UNR) {
+      u32x4 v[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int q = tid + (u0 + u) * Cfg::NT, r = q / CPR, c = q % CPR;
+        v[u] = *(const u32x4*)(pl + r * PITCH + ((c ^ (r & SWZ)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int q = tid + (u0 + u) * Cfg::NT, r = q / CPR, c = q % CPR;
+        const int64_t row = row0 + r;
+        const int col = col0 + c * 8;
+        if (row < row_lim && col < col_lim) *(u32x4*)(gbase + row * ld + col) = v[u];
+      }
     }
   };
-  __syncthreads();
+  lds_barrier();
 
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     // planes: h, then act's gate half, then act's up half
@@ -554,7 +633,7 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
     for (int pl = 0; pl < nplanes; ++pl) {
 #pragma unroll
       for (int part = 0; part < NPART; ++part) {
-        if (pl + part > 0) __syncthreads();
+        if (pl + part > 0) lds_barrier();
 #pragma unroll
         for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -562,86 +641,89 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int c = pcol(j, g) - part * PC;
-              if (c < 0 || c >= PC) continue;
+              if (!in_part(c)) continue;
               const f32x16& G = acc[i][j];
               const f32x16& U = acc[i][j + WN / 2];
               float v[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const float gt = G[4 * g + q], up = U[4 * g + q];
-                v[q] = pl == 0 ? gt / (1.0f + expf(-gt)) * up : (pl == 1 ? gt : up);
+                v[q] = pl == 0 ? gt * sigmoid_fast(gt) * up : (pl == 1 ? gt : up);
               }
-              put4(a_base[i] + mrow, c, v[0], v[1], v[2], v[3]);
+              put4(plane, a_base[i] + mrow, c, v[0], v[1], v[2], v[3]);
             }
         if (pl == 0)
-          store_plane(a.C, a.ldc, m0, seg_hi, n0 + part * PC, a.F);
+          store_plane(plane, a.C, a.ldc, m0, seg_hi, n0 + part * PC, a.F);
         else
-          store_plane(a.C2 + (pl == 2 ? a.F : 0), 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);
+          store_plane(plane, a.C2 + (pl == 2 ? a.F : 0), 2 * (int64_t)a.F, m0, seg_hi,
+                      n0 + part * PC, a.F);
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // acc = dh[row][f].  The forward's act rows ([gate | up], bf16) for this
-    // tile are first copied into LDS with coalesced 16-byte loads (gate plane,
-    // then up plane).  Each lane reads its own gate/up values from LDS, turns
-    // dh into dgate in place, and writes dup over its own gate slots (each slot
-    // has exactly one reader), so the gate plane becomes the dup plane; both
-    // results then leave through the plane path into dact's two halves.
-    static_assert(NPART == 1, "SwiGLU backward runs on tiles whose act planes fit LDS");
-    static_assert(2 * BM * PITCH <= Cfg::LDS_BYTES, "gate and up planes must fit the ring");
+    // acc = dh[row][f].  Per part (a PC-column slice of the tile), the
+    // forward's act values ([gate | up] rows, bf16) are first copied into two
+    // LDS planes with coalesced 16-byte loads.  Each lane reads its own gate/up
+    // values from LDS, turns dh into dgate in place, and writes dup over its own
+    // gate slots (each slot has exactly one reader), so the gate plane becomes
+    // the dup plane; both results then leave through the plane path into
+    // dact's two halves.
     uint8_t* gplane = smem;
     uint8_t* uplane = smem + BM * PITCH;
-    {
-      constexpr int CPR = PC / 8;
-      for (int q = tid; q < 2 * BM * CPR; q += Cfg::NT) {
-        const int half = q / (BM * CPR), rq = q % (BM * CPR);
-        const int r = rq / CPR, c = rq % CPR;
-        const int64_t row = m0 + r;
-        const int f = n0 + c * 8;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (row < seg_hi && f < a.F) v = *(const u32x4*)(a.aux + row * (int64_t)(2 * a.F) + half * a.F + f);
-        *(u32x4*)((half ? uplane : gplane) + r * PITCH + c * 16) = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int m = a_base[i] + mrow, c = pcol(j, g);
-          const u32x2 gw = *(const u32x2*)(gplane + m * PITCH + c * 2);
-          const u32x2 uw = *(const u32x2*)(uplane + m * PITCH + c * 2);
-          const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
-          const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
-          float du[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dh = acc[i][j][4 * g + q];
-            const float sg = 1.0f / (1.0f + expf(-gt[q]));
-            acc[i][j][4 * g + q] = dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg)));
-            du[q] = dh * gt[q] * sg;
-          }
-          put4(m, c, du[0], du[1], du[2], du[3]);  // plane == gplane
-        }
-    store_plane(a.C + a.F, 2 * (int64_t)a.F, m0, seg_hi, n0, a.F);  // dup half
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          put4(a_base[i] + mrow, pcol(j, g), acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
-               acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-    store_plane(a.C, 2 * (int64_t)a.F, m0, seg_hi, n0, a.F);  // dgate half
-  } else {  // EPI_STORE
-    uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
-    const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
-    const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
-      if (part > 0) __syncthreads();
+      if (part > 0) lds_barrier();
+      {
+        // act rows -> the two planes by LDS-DMA: every 1 KB region of a plane
+        // is one wave-level load, each lane fetching the chunk that belongs at
+        // its slot of the swizzled layout; rows past the segment and columns
+        // past F read as zeros
+        constexpr int RPRG = 1024 / PITCH;               // plane rows per region
+        constexpr int REGIONS = 2 * BM * PITCH / 1024;   // both planes
+        static_assert(RPRG * CPR == 64 && REGIONS % NW == 0, "act regions");
+        const int rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+        const u32x4 rAct = make_rsrc(a.aux + m0 * (int64_t)(2 * a.F),
+                                     (uint32_t)(rows_valid * 2 * a.F * 2));
+#pragma unroll
+        for (int k = 0; k < REGIONS / NW; ++k) {
+          const int q = k * NW + wave;                   // region
+          const int half = q / (REGIONS / 2);
+          const int r = (q % (REGIONS / 2)) * RPRG + lane / CPR;
+          const int c = (lane % CPR) ^ (r & SWZ);
+          const int f = n0 + part * PC + c * 8;
+          const uint32_t voff = (r < rows_valid && f < a.F)
+                                    ? (uint32_t)((r * 2 * a.F + half * a.F + f) * 2)
+                                    : kOOB;
+          dma16(rAct, lds_addr(smem) + q * 1024, voff);
+        }
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int m = a_base[i] + mrow, c = pcol(j, g) - part * PC;
+            if (!in_part(c)) continue;
+            const u32x2 gw = *(const u32x2*)(gplane + poff(m, c));
+            const u32x2 uw = *(const u32x2*)(uplane + poff(m, c));
+            const float gt[4] = {lo_bf16(gw[0]), hi_bf16(gw[0]), lo_bf16(gw[1]), hi_bf16(gw[1])};
+            const float up[4] = {lo_bf16(uw[0]), hi_bf16(uw[0]), lo_bf16(uw[1]), hi_bf16(uw[1])};
+            float du[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float dh = acc[i][j][4 * g + q];
+              const float sg = sigmoid_fast(gt[q]);
+              acc[i][j][4 * g + q] = dh * up[q] * (sg * (1.0f + gt[q] * (1.0f - sg)));
+              du[q] = dh * gt[q] * sg;
+            }
+            put4(gplane, m, c, du[0], du[1], du[2], du[3]);
+            // one group at a time: keeps the LDS reads from all being hoisted
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      store_plane(gplane, a.C + a.F, 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);  // dup
+      lds_barrier();
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -649,11 +731,31 @@ __global__ void __launch_bounds__(Cfg::NT) grouped_gemm_kernel(Args a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int c = pcol(j, g) - part * PC;
-            if (c < 0 || c >= PC) continue;
-            put4(a_base[i] + mrow, c, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+            if (!in_part(c)) continue;
+            put4(gplane, a_base[i] + mrow, c, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
                  acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
           }
-      store_plane(Cg, a.ldc, row0, rows_lim, n0 + part * PC, a.N);
+      store_plane(gplane, a.C, 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);  // dgate
+    }
+  } else {  // EPI_STORE
+    uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
+    const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
+    const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) {
+      if (part > 0) lds_barrier();
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = pcol(j, g) - part * PC;
+            if (!in_part(c)) continue;
+            put4(plane, a_base[i] + mrow, c, acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                 acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          }
+      store_plane(plane, Cg, a.ldc, row0, rows_lim, n0 + part * PC, a.N);
     }
   }
 }
@@ -751,9 +853,9 @@ hipError_t launch_gemm_wgrad_down(int G, int64_t m_rows, int H, int F, const int
   a.offsets = offsets; a.counts = counts;
   a.m_rows = m_rows; a.M = H; a.N = F; a.F = F;
   a.lda = H; a.ldb = F; a.ldc = F; a.strideB = 0; a.strideC = (int64_t)H * F;
-  a.n_mtiles = (H + CfgWide::BM - 1) / CfgWide::BM; a.n_ntiles = (F + CfgWide::BN - 1) / CfgWide::BN;
+  a.n_mtiles = (H + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (F + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
-  return launch<CfgWide, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
 }
 
 // dW1[g] [2F,H] = dact_g^T [2F, rows] . x_rows_g [rows, H]
@@ -765,9 +867,9 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.offsets = offsets; a.counts = counts;
   a.m_rows = m_rows; a.M = 2 * F; a.N = H; a.F = F;
   a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = 0; a.strideC = (int64_t)2 * F * H;
-  a.n_mtiles = (2 * F + CfgWide::BM - 1) / CfgWide::BM; a.n_ntiles = (H + CfgWide::BN - 1) / CfgWide::BN;
+  a.n_mtiles = (2 * F + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (H + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
-  return launch<CfgWide, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
 }
 
 }  // namespace moe
