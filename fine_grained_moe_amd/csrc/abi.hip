@@ -66,6 +66,11 @@ int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K) {
   return capacity(T, E, K);
 }
 
+size_t moe_route_workspace_bytes(int32_t H, int32_t E) {
+  if (H <= 0 || E <= 0 || E > 128) return 0;
+  return moe::route_workspace_bytes(H, E);
+}
+
 size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
   (void)K;
   if (T < 0 || E <= 0) return 0;
@@ -79,13 +84,15 @@ size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K)
 
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
                        const float* w_router, const float* bias, int32_t* topk_idx,
-                       float* topk_w, float* topk_s, void* stream) {
+                       float* topk_w, float* topk_s, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_dims(__func__, T, H, E, K);
   if (st) return st;
   if (T == 0) return MOE_OK;
   REQUIRE(x && w_router && bias && topk_idx && topk_w, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(ws != nullptr && ws_bytes >= moe_route_workspace_bytes(H, E),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   return hip_status(moe::launch_route(T, H, E, K, x, w_router, bias, topk_idx, topk_w, topk_s,
-                                      (hipStream_t)stream),
+                                      ws, (hipStream_t)stream),
                     __func__);
 }
 

@@ -41,9 +41,12 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace gemm {
+
+using namespace lds;
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MINB_>
 struct TileCfg {
@@ -91,6 +94,13 @@ struct TileCfg {
 // 64-deep k stages (128-byte row segments per load)
 using CfgRows =
     TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, MOE_ROWS_WGM, MOE_ROWS_WGN, MOE_ROWS_MINB>;
+// row tiles for the products whose columns are the hidden size H (down
+// forward, gate/up data gradient): 0 = CfgRows, 1 = 128 x 512 tiles of 8 waves
+// (wave tile 64 x 128), two 64-deep stages
+#ifndef MOE_ROWS_H
+#define MOE_ROWS_H 0
+#endif
+using CfgRowsH = std::conditional_t<MOE_ROWS_H != 0, TileCfg<128, 512, 64, 2, 2, 4, 1>, CfgRows>;
 // 256 x 256 tiles of 8 waves (wave tile 128 x 64), one workgroup per CU
 using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4, 1>;
 // tile of the K-grouped weight-gradient products: 0 = CfgWide, 1 = CfgRows
@@ -130,109 +140,6 @@ struct Args {
   int n_mtiles, n_ntiles, G;
 };
 
-// --------------------------------------------------------------------------
-// Global -> LDS: buffer loads straight into LDS (buffer_load_dwordx4 ... lds)
-// --------------------------------------------------------------------------
-// Each wave-level load moves 64 lanes x 16 B = 1 KB into a contiguous LDS
-// region whose base is wave-uniform (M0); lane l lands at base + 16*l.  The
-// LDS swizzle is therefore applied on the global side: lane l fetches the
-// global chunk that belongs at its LDS slot.  A lane whose element is out of
-// range (rows past the segment, k past K, columns past N) gets an offset past
-// the buffer's num_records, which the hardware turns into zeros (checked per
-// dword), so masked rows and tails contribute exactly nothing.
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
-
-// raw buffer resource: base, stride 0, num_records = bytes.  The arguments
-// are workgroup-uniform; readfirstlane makes that explicit so the descriptor
-// lives in SGPRs, as the buffer instruction requires.
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)base;
-  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
-               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
-               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3};
-}
-
-// One wave-level global -> LDS load of 64 x 16 B.  lds: wave-uniform LDS byte
-// address of the 1 KB destination.  Issued from inline asm so that the compiler
-// does not treat the LDS writes as aliasing every later LDS read (it would put
-// a wait for all outstanding loads before each transposing read); the kernel
-// orders them itself with explicit vmcnt waits and barriers.  M0 is used by
-// nothing else in these kernels.
-__device__ __forceinline__ void dma16(const u32x4& rs, uint32_t lds, uint32_t voff) {
-  lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds), "v"(voff), "s"(rs)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// s_waitcnt vmcnt(n) leaving expcnt/lgkmcnt unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-  asm volatile("" ::: "memory");
-}
-
-// wait until at most `ahead` stages of LOADS loads each are still in flight
-template <int LOADS, int MAXA>
-__device__ __forceinline__ void wait_stages(int ahead) {
-  if constexpr (MAXA <= 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (ahead >= MAXA) wait_vmcnt<LOADS * MAXA>();
-    else wait_stages<LOADS, MAXA - 1>(ahead);
-  }
-}
-
-// every wave's LDS reads done, then a workgroup barrier that orders memory
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int BK>
-__device__ __forceinline__ int kc_swz(int r) {
-  return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-}
-
-// K-contig tile of R rows x BK k.  A 1 KB region holds RPR consecutive rows.
-template <int R, int BK, int NW>
-struct KcLoad {
-  static constexpr int CPR = BK / 8;           // 16-byte chunks per row
-  static constexpr int RPR = 1024 / (BK * 2);  // rows per region
-  static constexpr int PER = R / RPR / NW;     // regions per wave
-  static_assert(PER * RPR * NW == R, "tile rows");
-  uint32_t off[PER];  // byte offset of the lane's chunk at kt = 0, or kOOB
-  int kel[PER];       // k offset (elements) of the lane's chunk within a stage
-  template <class RowOff>
-  __device__ __forceinline__ void init(RowOff row_off, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = i * NW + wave;
-      const int r = q * RPR + lane / CPR;
-      const int c = (lane % CPR) ^ kc_swz<BK>(r);
-      const uint32_t ro = row_off(r);
-      off[i] = ro == kOOB ? kOOB : ro + c * 16;
-      kel[i] = c * 8;
-    }
-  }
-  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t lds, int wave, int i, int kt,
-                                        int K) const {
-    const int q = i * NW + wave;
-    const bool kin = kt * BK + kel[i] < K;
-    const uint32_t v = (off[i] == kOOB || !kin) ? kOOB : off[i] + (uint32_t)kt * (BK * 2);
-    dma16(rs, lds + q * 1024, v);
-  }
-};
-
 // MN-contig tile of BK k-rows x C columns.  A 1 KB region holds KPR k-rows.
 template <int C, int BK, int NW>
 struct McLoad {
@@ -267,13 +174,6 @@ struct McLoad {
 // --------------------------------------------------------------------------
 // LDS -> fragment: lane l gets Op[mn = base + l%32][k = 16*kk + 8*(l/32) + 0..7]
 // --------------------------------------------------------------------------
-template <int BK>
-__device__ __forceinline__ bf16x8 frag_kc(const uint8_t* lds, int base, int kk, int lane) {
-  const int row = base + (lane & 31);
-  const int c = 2 * kk + (lane >> 5);
-  return *(const bf16x8*)(lds + row * (BK * 2) + ((c ^ kc_swz<BK>(row)) << 4));
-}
-
 // LDS address of the first of the two transposing reads that build lane l's
 // fragment of an MN-contig tile; the second read is 4 k-rows (8*C bytes) on.
 template <int C>
@@ -770,16 +670,16 @@ static hipError_t launch(const Args& a, int nblocks, hipStream_t s) {
 
 // M-grouped launch: routed segments use the 128-row tile (= alignment), the
 // dense single group (shared experts) the 256-row tile
-template <int ASRC, int BSRC, int EPI>
+template <int ASRC, int BSRC, int EPI, class CR = CfgRows>
 static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_tile_wide, int ncols,
                               hipStream_t s) {
-  // routed segments need the 128-row tile (= alignment); the SwiGLU-backward
-  // epilogue stages two act planes in LDS, which only the 128-row tile leaves
-  // room for; everything else dense takes the 256-row tile
+  // routed segments need 128-row tiles (= alignment); the SwiGLU-backward
+  // epilogue keeps two act planes in LDS, which the 128-row tile has room
+  // for; everything else dense takes the 256-row tile
   auto rows = [&]() {
-    a.n_mtiles = (int)((a.m_rows + CfgRows::BM - 1) / CfgRows::BM);
+    a.n_mtiles = (int)((a.m_rows + CR::BM - 1) / CR::BM);
     a.n_ntiles = (ncols + n_cols_per_tile_rows - 1) / n_cols_per_tile_rows;
-    return launch<CfgRows, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
+    return launch<CR, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
   };
   if constexpr (EPI == EPI_SWIGLU_BWD) {
     return rows();
@@ -817,7 +717,7 @@ hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* 
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = F; a.F = F;
   a.lda = F; a.ldb = F; a.ldc = H; a.strideB = (int64_t)H * F; a.G = G;
-  return launch_rows<KC, KC, EPI_STORE>(a, CfgRows::BN, CfgWide::BN, H, s);
+  return launch_rows<KC, KC, EPI_STORE, CfgRowsH>(a, CfgRowsH::BN, CfgWide::BN, H, s);
 }
 
 hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
@@ -841,7 +741,7 @@ hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = 2 * F; a.F = F;
   a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = (int64_t)2 * F * H; a.G = G;
-  return launch_rows<KC, MC, EPI_STORE>(a, CfgRows::BN, CfgWide::BN, H, s);
+  return launch_rows<KC, MC, EPI_STORE, CfgRowsH>(a, CfgRowsH::BN, CfgWide::BN, H, s);
 }
 
 // dW2[g] [H,F] = dy_rows_g^T [H, rows] . h_g [rows, F]

@@ -8,9 +8,10 @@ namespace moe {
 
 constexpr int kAlign = 128;  // grouped-GEMM row tile = segment alignment
 
+size_t route_workspace_bytes(int H, int E);
 hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
-                        hipStream_t s);
+                        void* ws, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,

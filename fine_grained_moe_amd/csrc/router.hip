@@ -1,16 +1,28 @@
-// Router of the MoE layer on gfx950: FP32 gating GEMV, sigmoid scores,
-// bias-adjusted top-K selection and normalised combine weights, one kernel.
+// Router of the MoE layer on gfx950: FP32 gating projection, sigmoid scores,
+// bias-adjusted top-K selection and normalised combine weights.
 //
 // "dots.llm1 Technical Report" summary page, section "Method": the gating
 // projection runs in FP32 for stable routing decisions; balancing uses the
 // DeepSeek auxiliary-loss-free bias; top-6 of 128 routed experts.  Model card
 // "Model Architecture Features": balancing through dynamic bias terms.
 //
-// Work split: a 256-thread workgroup owns 32 tokens and all E <= 128 experts;
-// each thread holds a 4-token x 4-expert block of fp32 accumulators.  The H
-// loop stages 32-wide slices of x (converted to fp32, transposed) and of
-// W_r in LDS.  Summation is blocked (32-term partial sums, 16 partials per
-// second-level sum) so the fp32 logit stays within ~1e-6 of the exact value.
+// Projection on the matrix cores, exactly in fp32 terms.  x is bf16, so each
+// fp32 router weight w is split into three bf16 parts w = hi + mid + lo
+// (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid); each difference
+// is exact in fp32 and the three parts carry w's 24-bit significand).  Every
+// product x * part is exact in the MFMA's fp32 accumulator, so
+//   logit = sum_h x[h] * (hi + mid + lo)[h]
+// is the fp32 dot product up to accumulation rounding.  The accumulation is
+// blocked (per lane, each 32x32 block sums 16 stages of 32 h, then adds into a
+// running fp32 total) so the logit stays within a few 1e-7 of the exact value.
+//
+// split_kernel writes the three parts in MFMA fragment order (one 1 KB block
+// per part, 32-expert block and 16-deep k-step: lane l's 16 bytes are the
+// eight k of expert l%32 at k offset 8*(l/32)), so every operand load is one
+// contiguous 1 KB LDS-DMA.  route_kernel: a 256-thread workgroup owns 64
+// tokens and all E <= 128 experts; wave w computes the 64 x 32 logit block of
+// experts 32w.., with x tiles (K-contiguous, swizzled) and weight fragments
+// streamed into a 5-stage LDS ring.
 //
 // Selection: one wave per token; lane l owns experts l and l+64.  Keys
 // v = s + b are turned into order-preserving 32-bit codes (NaN -> -inf) and
@@ -18,11 +30,26 @@
 // largest key and, among equal keys, the lowest index.  K rounds.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace router {
 
-constexpr int NT = 256, TB = 32, HC = 32, EMAX = 128;
+using namespace lds;
+
+constexpr int NT = 256, NW = 4, TB = 64, BK = 32, STAGES = 5, EMAX = 128, EBMAX = EMAX / 32;
+constexpr int KK = BK / 16;                                   // k-steps per stage
+constexpr int A_BYTES = TB * BK * 2;                          // x tile
+constexpr int B_REGIONS = 3 * EBMAX * KK;                     // weight fragments per stage
+constexpr int STAGE_BYTES = A_BYTES + B_REGIONS * 1024;
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+constexpr int A_PER = KcLoad<TB, BK, NW>::PER;                // x regions per wave
+constexpr int B_PER = B_REGIONS / NW;                         // weight regions per wave
+constexpr int LOADS = A_PER + B_PER;
+constexpr int SUM_BLOCK = 16;                                 // stages per partial sum
+static_assert(B_REGIONS % NW == 0, "weight regions per wave");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(TB * (EMAX + 1) * 4 <= LDS_BYTES, "logit tile fits the ring");
 
 __device__ __forceinline__ uint32_t order_code(float v) {
   if (v != v) v = -__builtin_inff();  // NaN ranks lowest
@@ -41,117 +68,141 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-__global__ void __launch_bounds__(NT) route_kernel(int T, int H, int E, int K,
-                                                   const uint16_t* __restrict__ x,
-                                                   const float* __restrict__ w,
-                                                   const float* __restrict__ bias,
-                                                   int32_t* __restrict__ topk_idx,
-                                                   float* __restrict__ topk_w,
-                                                   float* __restrict__ topk_s) {
-  __shared__ __attribute__((aligned(16))) float xs[2][HC][TB];      // [h][t]
-  __shared__ __attribute__((aligned(16))) float ws[2][HC][EMAX];    // [h][e]
-  __shared__ float lg[TB][EMAX + 1];
-
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * TB;
-  const int eg = tid & 31, tg = tid >> 5;  // experts eg*4.., tokens tg*4..
-
-  // staging: x slice 32 tokens x 32 h bf16 = 1024 values -> 4 per thread
-  //          w slice 32 h x 128 e fp32 = 4096 values -> 16 per thread (4 x float4)
-  const int xt = tid >> 3, xh = (tid & 7) * 4;  // token, h offset (4 bf16)
-  uint32_t xr[2];
-  f32x4 wr[4];
-
-  auto load = [&](int h0) {
-    const int t = t0 + xt;
-    if (t < T) {
-      const uint32_t* p = (const uint32_t*)(x + (int64_t)t * H + h0 + xh);
-      xr[0] = p[0];
-      xr[1] = p[1];
-    } else {
-      xr[0] = xr[1] = 0;
+// wf[p][eb][ks][lane][8]: part p of w_router[16 ks + 8 (lane/32) + j][32 eb + lane%32]
+__global__ void __launch_bounds__(64) split_kernel(int H, int E, const float* __restrict__ w,
+                                                   uint16_t* __restrict__ wf) {
+  const int lane = threadIdx.x;
+  const int ks = blockIdx.x, eb = blockIdx.y;
+  const int nks = H / 16, EB = gridDim.y;
+  const int e = 32 * eb + (lane & 31);
+  const int k0 = 16 * ks + 8 * (lane >> 5);
+  uint32_t part[3][4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    float v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) v[q] = e < E ? w[(int64_t)(k0 + j + q) * E + e] : 0.f;
+    uint16_t b[3][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint16_t hi = f32_to_bf16(v[q]);
+      const float r1 = v[q] - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(mid);
+      b[0][q] = hi;
+      b[1][q] = mid;
+      b[2][q] = f32_to_bf16(r2);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int q = tid + i * NT;          // 0..1023 float4 slots: h = q/32, e4 = q%32
-      int hh = q >> 5, e4 = (q & 31) * 4;
-      if (e4 < E) {
-        const float* p = w + (int64_t)(h0 + hh) * E + e4;
-        if (e4 + 4 <= E && (E & 3) == 0) {
-          wr[i] = *(const f32x4*)p;
-        } else {
-          for (int c = 0; c < 4; ++c) wr[i][c] = (e4 + c < E) ? p[c] : 0.f;
-        }
-      } else {
-        wr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    xs[buf][xh + 0][xt] = lo_bf16(xr[0]);
-    xs[buf][xh + 1][xt] = hi_bf16(xr[0]);
-    xs[buf][xh + 2][xt] = lo_bf16(xr[1]);
-    xs[buf][xh + 3][xt] = hi_bf16(xr[1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int q = tid + i * NT;
-      *(f32x4*)&ws[buf][q >> 5][(q & 31) * 4] = wr[i];
-    }
-  };
-
-  float s2[4][4], s1[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) s2[a][b] = s1[a][b] = 0.f;
-
-  const int nch = H / HC;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int cur = c & 1;
-    if (c + 1 < nch) load((c + 1) * HC);
-    float p[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) p[a][b] = 0.f;
-#pragma unroll 8
-    for (int hh = 0; hh < HC; ++hh) {
-      f32x4 xv = *(const f32x4*)&xs[cur][hh][tg * 4];
-      f32x4 wv = *(const f32x4*)&ws[cur][hh][eg * 4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) p[a][b] = __builtin_fmaf(xv[a], wv[b], p[a][b]);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) s1[a][b] += p[a][b];
-    if ((c & 15) == 15 || c + 1 == nch) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          s2[a][b] += s1[a][b];
-          s1[a][b] = 0.f;
-        }
-    }
-    if (c + 1 < nch) store(cur ^ 1);
-    __syncthreads();
+    for (int p = 0; p < 3; ++p) part[p][j / 2] = (uint32_t)b[p][0] | ((uint32_t)b[p][1] << 16);
   }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int64_t blk = ((int64_t)p * EB + eb) * nks + ks;
+    *(u32x4*)(wf + blk * 512 + lane * 8) = u32x4{part[p][0], part[p][1], part[p][2], part[p][3]};
+  }
+}
 
+__global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K,
+                                                      const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ wf,
+                                                      const float* __restrict__ bias,
+                                                      int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_w,
+                                                      float* __restrict__ topk_s) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * TB;
+  const int EB = (E + 31) / 32, nks = H / 16, nk = H / BK;
+
+  // operand sources: x rows t0.. (rows past T read as zeros), weight fragments
+  const int rows_valid = min(TB, T - t0);
+  const u32x4 rX = make_rsrc(x + (int64_t)t0 * H, (uint32_t)(rows_valid * H * 2));
+  const u32x4 rW = make_rsrc(wf, (uint32_t)(3 * EB * nks * 1024));
+  KcLoad<TB, BK, NW> lx;
+  lx.init([&](int r) -> uint32_t { return r < rows_valid ? (uint32_t)(r * H * 2) : kOOB; }, wave,
+          lane);
+  const uint32_t smem_base = lds_addr(smem);
+  auto issue = [&](int kt) {
+    const uint32_t As = smem_base + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < A_PER; ++i) lx.issue(rX, As, wave, i, kt, H);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) lg[tg * 4 + a][eg * 4 + b] = s2[a][b];
-  __syncthreads();
+    for (int i = 0; i < B_PER; ++i) {
+      const int r = i * NW + wave;                 // region: part, expert block, k-step
+      const int p = r / (EBMAX * KK), eb = (r / KK) % EBMAX, kl = r % KK;
+      const int ks = kt * KK + kl;
+      const uint32_t off = (eb < EB && ks < nks)
+                               ? (uint32_t)((((p * EB + eb) * nks) + ks) * 1024 + lane * 16)
+                               : kOOB;
+      dma16(rW, As + A_BYTES + r * 1024, off);
+    }
+  };
+
+  f32x16 acc[2], tot[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = tot[i][r] = 0.f;
+  const bool active = wave < EB;
+
+  // branch-free ring: loads past the last stage read as zeros
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<LOADS * (STAGES - 2)>();
+    lds_barrier();
+    issue(kt + STAGES - 1);  // into the buffer every wave finished reading
+    const uint8_t* As = smem + (kt % STAGES) * STAGE_BYTES;
+    const uint8_t* Bs = As + A_BYTES;
+    if (active) {
+      bf16x8 af[KK][2], bq[KK][3];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[kk][i] = frag_kc<BK>(As, 32 * i, kk, lane);
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          bq[kk][p] = *(const bf16x8*)(Bs + ((p * EBMAX + wave) * KK + kk) * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk][p], af[kk][i], acc[i], 0, 0, 0);
+    }
+    if ((kt % SUM_BLOCK) == SUM_BLOCK - 1 || kt + 1 == nk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          tot[i][r] += acc[i][r];
+          acc[i][r] = 0.f;
+        }
+    }
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // logits -> LDS [token][expert]: lane holds token 32i + l%32 and experts
+  // 32w + 8(r/4) + 4(l/32) + r%4
+  float* lg = (float*)smem;
+  constexpr int LP = EMAX + 1;
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        lg[(32 * i + (lane & 31)) * LP + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] =
+            tot[i][r];
+  }
+  lds_barrier();
 
   // ---- selection: one wave per token ---------------------------------
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int tt = wave; tt < TB; tt += NT / 64) {
+  for (int tt = wave; tt < TB; tt += NW) {
     const int t = t0 + tt;
     if (t >= T) break;
     float sc[2];
@@ -160,9 +211,9 @@ __global__ void __launch_bounds__(NT) route_kernel(int T, int H, int E, int K,
     for (int q = 0; q < 2; ++q) {
       const int e = lane + 64 * q;
       if (e < E) {
-        float z = lg[tt][e];
+        const float z = lg[tt * LP + e];
         sc[q] = 1.0f / (1.0f + expf(-z));
-        float v = sc[q] + bias[e];
+        const float v = sc[q] + bias[e];
         key[q] = ((uint64_t)order_code(v) << 32) | (uint32_t)(0xFFFFu - e);
       } else {
         sc[q] = 0.f;
@@ -198,12 +249,21 @@ __global__ void __launch_bounds__(NT) route_kernel(int T, int H, int E, int K,
 
 }  // namespace router
 
+size_t route_workspace_bytes(int H, int E) {
+  return (size_t)3 * ((E + 31) / 32) * 32 * (size_t)H * 2;
+}
+
 hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
-                        hipStream_t s) {
+                        void* ws, hipStream_t s) {
+  uint16_t* wf = (uint16_t*)ws;
+  hipLaunchKernelGGL(router::split_kernel, dim3(H / 16, (E + 31) / 32), dim3(64), 0, s, H, E,
+                     w_router, wf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || T == 0) return e;
   const int nb = (T + router::TB - 1) / router::TB;
-  hipLaunchKernelGGL(router::route_kernel, dim3(nb), dim3(router::NT), 0, s, T, H, E, K, x,
-                     w_router, bias, topk_idx, topk_w, topk_s);
+  hipLaunchKernelGGL(router::route_kernel, dim3(nb), dim3(router::NT), 0, s, T, H, E, K, x, wf,
+                     bias, topk_idx, topk_w, topk_s);
   return hipGetLastError();
 }
 

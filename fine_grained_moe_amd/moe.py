@@ -27,9 +27,10 @@ _SIGS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_align": (_i32, []),
     "moe_capacity_rows": (_i64, [_i32, _i32, _i32]),
+    "moe_route_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
-    "moe_route": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_route": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute": (_i32, [_i32, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
                            _p, _sz, _p]),
     "moe_grouped_swiglu_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -97,6 +98,10 @@ def moe_capacity_rows(T: int, E: int, K: int) -> int:
     return int(_lib.moe_capacity_rows(T, E, K))
 
 
+def moe_route_workspace_bytes(H: int, E: int) -> int:
+    return int(_lib.moe_route_workspace_bytes(H, E))
+
+
 def moe_permute_workspace_bytes(T: int, E: int, K: int) -> int:
     return int(_lib.moe_permute_workspace_bytes(T, E, K))
 
@@ -108,16 +113,19 @@ def moe_route_bwd_workspace_bytes(T: int, H: int, E: int, K: int) -> int:
 # ---------------------------------------------------------------------------
 # entry points (outputs allocated when not given)
 # ---------------------------------------------------------------------------
-def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None):
+def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=None):
     T, H = x.shape
     E = w_router.shape[1]
     dev = x.device
     topk_idx = torch.empty((T, K), dtype=I32, device=dev) if topk_idx is None else topk_idx
     topk_w = torch.empty((T, K), dtype=F32, device=dev) if topk_w is None else topk_w
     topk_s = torch.empty((T, K), dtype=F32, device=dev) if topk_s is None else topk_s
+    if ws is None:
+        ws = torch.empty(max(moe_route_workspace_bytes(H, E), 1), dtype=torch.uint8, device=dev)
     _check(_lib.moe_route(T, H, E, K, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                           _ptr(bias, F32, "bias"), _ptr(topk_idx, I32, "topk_idx"),
-                          _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"), _stream()))
+                          _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"),
+                          _ptr(ws), ws.numel(), _stream()))
     return topk_idx, topk_w, topk_s
 
 

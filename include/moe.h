@@ -69,6 +69,10 @@ int32_t moe_align(void);
  * (x_rows, act, h, y_rows, dy_rows, dact, dx_rows) have this many rows. */
 int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K);
 
+/* host: bytes of the workspace moe_route needs, 3 * ceil(E/32)*32 * H * 2
+ * (0 for an invalid H or E). */
+size_t moe_route_workspace_bytes(int32_t H, int32_t E);
+
 /* host: bytes of the workspace moe_permute needs. */
 size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
 
@@ -90,10 +94,13 @@ size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K)
  *
  * x [T,H] bf16; w_router [H,E] fp32; bias [E] fp32;
  * topk_idx [T,K] int32; topk_w [T,K] fp32; topk_s [T,K] fp32 (nullable).
+ * ws: device workspace of at least moe_route_workspace_bytes(H,E) bytes (the
+ * router weight re-encoded for the matrix cores; rewritten by every call).
  */
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K,
                        const uint16_t* x, const float* w_router, const float* bias,
-                       int32_t* topk_idx, float* topk_w, float* topk_s, void* stream);
+                       int32_t* topk_idx, float* topk_w, float* topk_s,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_permute - token permutation into per-expert segments padded to `align`

@@ -46,6 +46,7 @@ def test_host_queries(lib):
     lib.moe_capacity_rows.restype = ctypes.c_int64
     lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_route_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_status_string.restype = ctypes.c_char_p
     assert lib.moe_align() == 128
     # ceil((T*K + E*127)/128)*128
@@ -53,6 +54,9 @@ def test_host_queries(lib):
     assert lib.moe_capacity_rows(256, 128, 6) == 17792
     assert lib.moe_capacity_rows(0, 8, 2) == 1024
     assert lib.moe_capacity_rows(-1, 8, 2) == -1
+    assert lib.moe_route_workspace_bytes(5120, 128) == 3 * 128 * 5120 * 2
+    assert lib.moe_route_workspace_bytes(64, 8) == 3 * 32 * 64 * 2
+    assert lib.moe_route_workspace_bytes(64, 0) == 0
     assert lib.moe_permute_workspace_bytes(8192, 128, 6) == 2 * 32 * 128 * 4
     assert lib.moe_permute_workspace_bytes(0, 128, 6) == 0
     assert lib.moe_route_bwd_workspace_bytes(8192, 5120, 128, 6) == 128 * 5120 * 4 + 65408 * 4
@@ -69,18 +73,21 @@ FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
 
 def test_route_rejects(lib):
     f = lib.moe_route
-    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7
-    ok = [_p(FAKE)] * 6 + [_p(None)]
-    assert f(8, 64, 8, 9, *ok) == 1          # K > E
-    assert f(8, 64, 8, 0, *ok) == 1          # K = 0
-    assert f(-1, 64, 8, 2, *ok) == 1         # T < 0
-    assert f(8, 96, 8, 2, *ok) == 2          # H % 64
-    assert f(8, 64, 200, 2, *ok) == 2        # E > 128
-    assert f(8, 64, 32, 17, *ok) == 2        # K > 16
-    assert f(8, 64, 8, 2, _p(None), *[_p(FAKE)] * 5, _p(None)) == 1  # null x
-    assert f(0, 64, 8, 2, *[_p(None)] * 7) == 0   # T = 0 no-op
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
+    big = 1 << 30
+    ok = [_p(FAKE)] * 6 + [_p(FAKE)]
+    assert f(8, 64, 8, 9, *ok, big, _p(None)) == 1          # K > E
+    assert f(8, 64, 8, 0, *ok, big, _p(None)) == 1          # K = 0
+    assert f(-1, 64, 8, 2, *ok, big, _p(None)) == 1         # T < 0
+    assert f(8, 96, 8, 2, *ok, big, _p(None)) == 2          # H % 64
+    assert f(8, 64, 200, 2, *ok, big, _p(None)) == 2        # E > 128
+    assert f(8, 64, 32, 17, *ok, big, _p(None)) == 2        # K > 16
+    assert f(8, 64, 8, 2, _p(None), *[_p(FAKE)] * 6, big, _p(None)) == 1  # null x
+    assert f(8, 64, 8, 2, *ok, 16, _p(None)) == 3           # workspace too small
+    assert f(8, 64, 8, 2, *[_p(FAKE)] * 6, _p(None), big, _p(None)) == 3  # no workspace
+    assert f(0, 64, 8, 2, *[_p(None)] * 7, 0, _p(None)) == 0   # T = 0 no-op
     lib.moe_last_error.restype = ctypes.c_char_p
-    f(8, 64, 8, 9, *ok)
+    f(8, 64, 8, 9, *ok, big, _p(None))
     assert b"K > E" in lib.moe_last_error()
 
 
