@@ -26,6 +26,10 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
                pack_bf16x2(f[6], f[7])};
 }
 
+// Every k-loop below is unrolled to KMAX with k < K guards, so a lane's K row
+// loads of one chunk are all in flight together; KMAX = 8 when K <= 8 keeps
+// the register count (and so the occupancy) of the common case low.
+template <int KMAX>
 __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
                                                      const uint16_t* __restrict__ y_rows,
                                                      const int32_t* __restrict__ row_of,
@@ -35,30 +39,35 @@ __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
   if (t >= T) return;
-  int rows[16];
-  float g[16];
-  for (int k = 0; k < K; ++k) {
-    rows[k] = row_of[(int64_t)t * K + k];
-    g[k] = topk_w[(int64_t)t * K + k];
+  int rows[KMAX];
+  float g[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    rows[k] = k < K ? row_of[(int64_t)t * K + k] : 0;
+    g[k] = k < K ? topk_w[(int64_t)t * K + k] : 0.f;
   }
   const int nchunk = H / 8;
   for (int c = lane; c < nchunk; c += 64) {
+    u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
+    if (y_shared) vs = ((const u32x4*)(y_shared + (int64_t)t * H))[c];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) vr[k] = ((const u32x4*)(y_rows + (int64_t)rows[k] * H))[c];
     float acc[8], v[8];
-    if (y_shared) {
-      unpack8(((const u32x4*)(y_shared + (int64_t)t * H))[c], acc);
-    } else {
+    unpack8(vs, acc);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    }
-    for (int k = 0; k < K; ++k) {
-      unpack8(((const u32x4*)(y_rows + (int64_t)rows[k] * H))[c], v);
+    for (int k = 0; k < KMAX; ++k) {
+      if (k < K) {
+        unpack8(vr[k], v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[k], v[i], acc[i]);
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[k], v[i], acc[i]);
+      }
     }
     ((u32x4*)(y + (int64_t)t * H))[c] = pack8(acc);
   }
 }
 
+template <int KMAX>
 __global__ void __launch_bounds__(NT) combine_bwd_kernel(int T, int H, int K,
                                                          const uint16_t* __restrict__ dy,
                                                          const uint16_t* __restrict__ y_rows,
@@ -69,28 +78,48 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(int T, int H, int K,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
   if (t >= T) return;
+  int rows[KMAX];
+  float g[KMAX], dot[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    rows[k] = k < K ? row_of[(int64_t)t * K + k] : 0;
+    g[k] = k < K ? topk_w[(int64_t)t * K + k] : 0.f;
+    dot[k] = 0.f;
+  }
   const int nchunk = H / 8;
-  for (int k = 0; k < K; ++k) {
-    const int row = row_of[(int64_t)t * K + k];
-    const float gk = topk_w[(int64_t)t * K + k];
-    float dot = 0.f;
-    for (int c = lane; c < nchunk; c += 64) {
-      float d[8], v[8], o[8];
-      unpack8(((const u32x4*)(dy + (int64_t)t * H))[c], d);
-      unpack8(((const u32x4*)(y_rows + (int64_t)row * H))[c], v);
+  for (int c = lane; c < nchunk; c += 64) {
+    const u32x4 vd = ((const u32x4*)(dy + (int64_t)t * H))[c];
+    u32x4 vr[KMAX];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        dot = __builtin_fmaf(d[i], v[i], dot);
-        o[i] = gk * d[i];
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) vr[k] = ((const u32x4*)(y_rows + (int64_t)rows[k] * H))[c];
+    float d[8], v[8], o[8];
+    unpack8(vd, d);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (k < K) {
+        unpack8(vr[k], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dot[k] = __builtin_fmaf(d[i], v[i], dot[k]);
+          o[i] = g[k] * d[i];
+        }
+        ((u32x4*)(dy_rows + (int64_t)rows[k] * H))[c] = pack8(o);
       }
-      ((u32x4*)(dy_rows + (int64_t)row * H))[c] = pack8(o);
     }
+  }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) dg[(int64_t)t * K + k] = dot;
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < K) {
+      float v = dot[k];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) dg[(int64_t)t * K + k] = v;
+    }
   }
 }
 
+template <int KMAX>
 __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
                                                            const uint16_t* __restrict__ dx_rows,
                                                            const int32_t* __restrict__ row_of,
@@ -100,31 +129,40 @@ __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
   if (t >= T) return;
-  int rows[16];
-  for (int k = 0; k < K; ++k) rows[k] = row_of[(int64_t)t * K + k];
+  int rows[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) rows[k] = k < K ? row_of[(int64_t)t * K + k] : 0;
   const int nchunk = H / 8;
   for (int c = lane; c < nchunk; c += 64) {
+    u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) vr[k] = ((const u32x4*)(dx_rows + (int64_t)rows[k] * H))[c];
+    if (dx_shared) vs = ((const u32x4*)(dx_shared + (int64_t)t * H))[c];
+    if (dx_router) {
+      const f32x4* p = (const f32x4*)(dx_router + (int64_t)t * H + (int64_t)c * 8);
+      a0 = p[0];
+      a1 = p[1];
+    }
     float acc[8], v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      unpack8(((const u32x4*)(dx_rows + (int64_t)rows[k] * H))[c], v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    if (dx_shared) {
-      unpack8(((const u32x4*)(dx_shared + (int64_t)t * H))[c], v);
+    for (int k = 0; k < KMAX; ++k) {
+      if (k < K) {
+        unpack8(vr[k], v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    if (dx_router) {
-      const f32x4* p = (const f32x4*)(dx_router + (int64_t)t * H + (int64_t)c * 8);
-      f32x4 a0 = p[0], a1 = p[1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += a0[i];
-        acc[4 + i] += a1[i];
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }
+    }
+    unpack8(vs, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += a0[i];
+      acc[4 + i] += a1[i];
     }
     ((u32x4*)(dx + (int64_t)t * H))[c] = pack8(acc);
   }
@@ -200,25 +238,57 @@ __global__ void __launch_bounds__(NT) route_bwd_token_kernel(int T, int H, int E
 }
 
 // dW_r[h,e] = sum over the valid rows r of e's segment of x_rows[r,h] * dl_row[r]
+// Workgroup (expert e, 512 columns): wave w takes the rows r0+w, r0+w+4, ...,
+// each lane 8 columns (one 16-byte chunk per row, four rows in flight); the
+// four partial sums are added in wave order through LDS, so the result does
+// not depend on timing.
+constexpr int WG_COLS = 512, WG_WAVES = 4, WG_UNROLL = 4;
 __global__ void __launch_bounds__(256) route_bwd_wgrad_kernel(int H, int E,
                                                               const uint16_t* __restrict__ x_rows,
                                                               const float* __restrict__ dl_row,
                                                               const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ counts,
                                                               float* __restrict__ dw) {
+  __shared__ float part[WG_WAVES - 1][WG_COLS];
   const int e = blockIdx.y;
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 2;
-  if (h >= H) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x * WG_COLS + lane * 8;
+  const bool hin = h < H;
   const int r0 = offsets[e], n = counts[e];
-  float a0 = 0.f, a1 = 0.f;
-  for (int r = r0; r < r0 + n; ++r) {
-    const float d = dl_row[r];
-    const uint32_t xv = *(const uint32_t*)(x_rows + (int64_t)r * H + h);
-    a0 = __builtin_fmaf(lo_bf16(xv), d, a0);
-    a1 = __builtin_fmaf(hi_bf16(xv), d, a1);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = wave; j < n; j += WG_WAVES * WG_UNROLL) {
+    u32x4 v[WG_UNROLL];
+    float d[WG_UNROLL];
+#pragma unroll
+    for (int u = 0; u < WG_UNROLL; ++u) {
+      const int jj = j + u * WG_WAVES;
+      const bool ok = jj < n && hin;
+      d[u] = jj < n ? dl_row[r0 + jj] : 0.f;
+      v[u] = ok ? *(const u32x4*)(x_rows + (int64_t)(r0 + jj) * H + h) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < WG_UNROLL; ++u) {
+      float xv[8];
+      unpack8(v[u], xv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(xv[i], d[u], acc[i]);
+    }
   }
-  dw[(int64_t)h * E + e] = a0;
-  dw[(int64_t)(h + 1) * E + e] = a1;
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[wave - 1][lane * 8 + i] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && hin) {
+#pragma unroll
+    for (int w = 0; w < WG_WAVES - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += part[w][lane * 8 + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dw[(int64_t)(h + i) * E + e] = acc[i];
+  }
 }
 
 }  // namespace comb
@@ -226,24 +296,39 @@ __global__ void __launch_bounds__(256) route_bwd_wgrad_kernel(int H, int E,
 hipError_t launch_combine(int T, int H, int K, const uint16_t* y_rows, const int32_t* row_of,
                           const float* topk_w, const uint16_t* y_shared, uint16_t* y,
                           hipStream_t s) {
-  hipLaunchKernelGGL(comb::combine_kernel, dim3((T + comb::TPB - 1) / comb::TPB), dim3(comb::NT), 0,
-                     s, T, H, K, y_rows, row_of, topk_w, y_shared, y);
+  const dim3 grid((T + comb::TPB - 1) / comb::TPB);
+  if (K <= 8)
+    hipLaunchKernelGGL(comb::combine_kernel<8>, grid, dim3(comb::NT), 0, s, T, H, K, y_rows, row_of,
+                       topk_w, y_shared, y);
+  else
+    hipLaunchKernelGGL(comb::combine_kernel<16>, grid, dim3(comb::NT), 0, s, T, H, K, y_rows, row_of,
+                       topk_w, y_shared, y);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(int T, int H, int K, const uint16_t* dy, const uint16_t* y_rows,
                               const int32_t* row_of, const float* topk_w, uint16_t* dy_rows,
                               float* dg, hipStream_t s) {
-  hipLaunchKernelGGL(comb::combine_bwd_kernel, dim3((T + comb::TPB - 1) / comb::TPB),
-                     dim3(comb::NT), 0, s, T, H, K, dy, y_rows, row_of, topk_w, dy_rows, dg);
+  const dim3 grid((T + comb::TPB - 1) / comb::TPB);
+  if (K <= 8)
+    hipLaunchKernelGGL(comb::combine_bwd_kernel<8>, grid, dim3(comb::NT), 0, s, T, H, K, dy, y_rows,
+                       row_of, topk_w, dy_rows, dg);
+  else
+    hipLaunchKernelGGL(comb::combine_bwd_kernel<16>, grid, dim3(comb::NT), 0, s, T, H, K, dy, y_rows,
+                       row_of, topk_w, dy_rows, dg);
   return hipGetLastError();
 }
 
 hipError_t launch_unpermute_add(int T, int H, int K, const uint16_t* dx_rows,
                                 const int32_t* row_of, const uint16_t* dx_shared,
                                 const float* dx_router, uint16_t* dx, hipStream_t s) {
-  hipLaunchKernelGGL(comb::unpermute_add_kernel, dim3((T + comb::TPB - 1) / comb::TPB),
-                     dim3(comb::NT), 0, s, T, H, K, dx_rows, row_of, dx_shared, dx_router, dx);
+  const dim3 grid((T + comb::TPB - 1) / comb::TPB);
+  if (K <= 8)
+    hipLaunchKernelGGL(comb::unpermute_add_kernel<8>, grid, dim3(comb::NT), 0, s, T, H, K, dx_rows,
+                       row_of, dx_shared, dx_router, dx);
+  else
+    hipLaunchKernelGGL(comb::unpermute_add_kernel<16>, grid, dim3(comb::NT), 0, s, T, H, K, dx_rows,
+                       row_of, dx_shared, dx_router, dx);
   return hipGetLastError();
 }
 
@@ -266,8 +351,8 @@ hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x_rows,
     hipLaunchKernelGGL(comb::route_bwd_token_kernel, dim3((T + comb::TPB - 1) / comb::TPB),
                        dim3(comb::NT), 0, s, T, H, E, K, wt, topk_idx, topk_s, dg, row_of, dl_row,
                        dx_router);
-  hipLaunchKernelGGL(comb::route_bwd_wgrad_kernel, dim3((H / 2 + 255) / 256, E), dim3(256), 0, s, H,
-                     E, x_rows, dl_row, offsets, counts, dw_router);
+  hipLaunchKernelGGL(comb::route_bwd_wgrad_kernel, dim3((H + comb::WG_COLS - 1) / comb::WG_COLS, E),
+                     dim3(256), 0, s, H, E, x_rows, dl_row, offsets, counts, dw_router);
   return hipGetLastError();
 }
 

@@ -6,9 +6,8 @@
 // bits, so their order cannot change a result):
 //   1. count   : per 256-token chunk, a histogram of the chunk's expert ids
 //   2. scan    : per expert, exclusive prefix over chunks (chunk bases) and the
-//                total count; padded exclusive scan over experts (offsets);
-//                the tile -> expert table; -1 into every padding row of
-//                src_token
+//                total count; padded exclusive scan over experts (offsets)
+//      fill    : -1 into every row of src_token; the tile -> expert table
 //   3. scatter : per chunk, each token's rank among the chunk's earlier
 //                tokens with the same expert (popcount of a per-expert token
 //                bitmask), so rows of a segment are in ascending token order
@@ -36,21 +35,26 @@ __global__ void __launch_bounds__(CH) count_kernel(int T, int E, int K,
   if (tid < E) chunk_counts[(int64_t)c * E + tid] = hist[tid];
 }
 
-__global__ void __launch_bounds__(1024) scan_kernel(int E, int nchunks, int align, int64_t m_cap,
+__global__ void __launch_bounds__(EMAX) scan_kernel(int E, int nchunks, int align,
                                                     const int32_t* __restrict__ chunk_counts,
                                                     int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ src_token,
-                                                    int32_t* __restrict__ tile_expert) {
+                                                    int32_t* __restrict__ offsets) {
   __shared__ int cnt[EMAX];
-  __shared__ int off[EMAX + 1];
   const int tid = threadIdx.x;
   if (tid < E) {
+    // exclusive prefix over chunks; eight independent loads per round
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      chunk_base[(int64_t)c * E + tid] = run;
-      run += chunk_counts[(int64_t)c * E + tid];
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunks) chunk_base[(int64_t)(c0 + u) * E + tid] = run;
+        run += v[u];
+      }
     }
     cnt[tid] = run;
     counts[tid] = run;
@@ -59,43 +63,37 @@ __global__ void __launch_bounds__(1024) scan_kernel(int E, int nchunks, int alig
   if (tid == 0) {
     int run = 0;
     for (int e = 0; e < E; ++e) {
-      off[e] = run;
+      offsets[e] = run;
       run += (cnt[e] + align - 1) / align * align;
     }
-    off[E] = run;
+    offsets[E] = run;
   }
+}
+
+// every row of src_token to -1 (the scatter then writes the token rows) and
+// the tile -> expert table (-1 past the last segment)
+__global__ void __launch_bounds__(256) fill_kernel(int E, int align, int64_t m_cap,
+                                                   const int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ src_token,
+                                                   int32_t* __restrict__ tile_expert) {
+  __shared__ int off[EMAX + 1];
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) off[i] = offsets[i];
   __syncthreads();
-  if (tid <= E) offsets[tid] = off[tid];
-  const int total = off[E];
-  const int ntiles = (int)(m_cap / align);
-  for (int i = tid; i < ntiles; i += blockDim.x) {
-    const int row = i * align;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= m_cap) return;
+  src_token[r] = -1;
+  if (r % align == 0) {
+    const int row = (int)r;
     int e = -1;
-    if (row < total) {
-      int lo = 0, hi = E - 1;  // last e with off[e] <= row and a non-empty segment
+    if (row < off[E]) {
+      int lo = 0, hi = E - 1;  // last e with off[e] <= row: a non-empty segment
       while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
+        const int mid = (lo + hi + 1) >> 1;
         if (off[mid] <= row) lo = mid; else hi = mid - 1;
       }
       e = lo;
     }
-    tile_expert[i] = e;
-  }
-  // padding rows inside segments and every row past the last segment
-  for (int64_t r = tid; r < m_cap; r += blockDim.x) {
-    const int ri = (int)r;
-    bool pad;
-    if (ri >= total) {
-      pad = true;
-    } else {
-      int lo = 0, hi = E - 1;
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= ri) lo = mid; else hi = mid - 1;
-      }
-      pad = ri >= off[lo] + cnt[lo];
-    }
-    if (pad) src_token[r] = -1;
+    tile_expert[r / align] = e;
   }
 }
 
@@ -166,8 +164,11 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
   if (nchunks > 0)
     hipLaunchKernelGGL(perm::count_kernel, dim3(nchunks), dim3(perm::CH), 0, s, T, E, K, topk_idx,
                        chunk_counts);
-  hipLaunchKernelGGL(perm::scan_kernel, dim3(1), dim3(1024), 0, s, E, nchunks, align, m_cap,
-                     chunk_counts, chunk_base, counts, offsets, src_token, tile_expert);
+  hipLaunchKernelGGL(perm::scan_kernel, dim3(1), dim3(perm::EMAX), 0, s, E, nchunks, align,
+                     chunk_counts, chunk_base, counts, offsets);
+  if (m_cap > 0)
+    hipLaunchKernelGGL(perm::fill_kernel, dim3((unsigned)((m_cap + 255) / 256)), dim3(256), 0, s, E,
+                       align, m_cap, offsets, src_token, tile_expert);
   if (nchunks > 0) {
     hipLaunchKernelGGL(perm::scatter_kernel, dim3(nchunks), dim3(perm::CH), 0, s, T, E, K,
                        topk_idx, chunk_base, offsets, row_of, src_token);
