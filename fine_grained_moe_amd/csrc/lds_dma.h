@@ -36,8 +36,14 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // a wait for all outstanding loads before each transposing read); the kernel
 // orders them itself with explicit vmcnt waits and barriers.  M0 is used by
 // nothing else in these kernels.
-__device__ __forceinline__ void dma16(const u32x4& rs, uint32_t lds, uint32_t voff) {
+__device__ __forceinline__ void dma16(const u32x4& rs_in, uint32_t lds, uint32_t voff) {
+  // both are workgroup-uniform; readfirstlane keeps them in SGPRs whatever
+  // the compiler concluded about their uniformity
   lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[0]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[1]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[2]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[3])};
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
