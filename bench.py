@@ -30,14 +30,14 @@ PEAK_HBM_GBS = 8000.0
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "2996fcdfc604aba6669d38037423b15cf8575f7788938ec60eb5e0bbcef74a74"
+TRAFFIC_SOURCE_SHA256 = "cce355c5c8f0c9a71a5e3b8311bb15ae04481654798837fef0b792423e701d80"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3127821.4, 405504.0), "down_fwd": (1179243.9, 491520.0),
-    "shared_gate_up_fwd": (348301.3, 135168.0), "shared_down_fwd": (180309.3, 81920.0),
-    "down_dgrad": (1504996.3, 270336.0), "gate_up_dgrad": (2420786.0, 491520.0),
-    "down_wgrad": (624304.0, 1802240.0), "gate_up_wgrad": (1124915.3, 3604480.0),
-    "shared_down_dgrad": (352415.5, 90112.0), "shared_gate_up_dgrad": (360540.8, 81920.0),
-    "shared_down_wgrad": (217183.4, 28160.0), "shared_gate_up_wgrad": (434272.2, 56320.0),
+    "gate_up_fwd": (3092372.0, 405504.0), "down_fwd": (1157367.5, 491520.0),
+    "shared_gate_up_fwd": (348239.8, 135168.0), "shared_down_fwd": (180287.4, 81920.0),
+    "down_dgrad": (1578507.5, 270336.0), "gate_up_dgrad": (2492468.0, 491520.0),
+    "down_wgrad": (591835.3, 1802240.0), "gate_up_wgrad": (1089884.3, 3604480.0),
+    "shared_down_dgrad": (352406.0, 90112.0), "shared_gate_up_dgrad": (360515.9, 81920.0),
+    "shared_down_wgrad": (217146.4, 28160.0), "shared_gate_up_wgrad": (434235.6, 56320.0),
 }
 
 
