@@ -685,8 +685,13 @@ static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_t
     return rows();
   } else {
     if (a.tile_expert) return rows();
-    a.n_mtiles = (int)((a.m_rows + CfgWide::BM - 1) / CfgWide::BM);
-    a.n_ntiles = (ncols + n_cols_per_tile_wide - 1) / n_cols_per_tile_wide;
+    const int mt = (int)((a.m_rows + CfgWide::BM - 1) / CfgWide::BM);
+    const int ntl = (ncols + n_cols_per_tile_wide - 1) / n_cols_per_tile_wide;
+    // few rows (decode-sized batches): the 256-row tile leaves most CUs idle,
+    // the 128-row tile doubles the workgroups
+    if (mt * ntl < 256) return rows();
+    a.n_mtiles = mt;
+    a.n_ntiles = ntl;
     return launch<CfgWide, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
   }
 }
