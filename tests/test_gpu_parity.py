@@ -186,6 +186,10 @@ MID = {
                                 router_std=0.1),
     # a single token
     "T1_H256_E32_K6": Workload("t1", T=1, H=256, E=32, K=6, S=2, F=64, seed=26, router_std=0.1),
+    # E not a multiple of 32 (a partial expert block in the router), H not a
+    # multiple of 128, F not a multiple of 64
+    "T700_H192_E48_K3_F160": Workload("odd", T=700, H=192, E=48, K=3, S=1, F=160, seed=27,
+                                      router_std=0.1),
 }
 
 
