@@ -13,16 +13,16 @@
 // product x * part is exact in the MFMA's fp32 accumulator, so
 //   logit = sum_h x[h] * (hi + mid + lo)[h]
 // is the fp32 dot product up to accumulation rounding.  The accumulation is
-// blocked (per lane, each 32x32 block sums 16 stages of 32 h, then adds into a
+// blocked (per lane, each 32x32 block sums 512 h at a time, then adds into a
 // running fp32 total) so the logit stays within a few 1e-7 of the exact value.
 //
 // split_kernel writes the three parts in MFMA fragment order (one 1 KB block
 // per part, 32-expert block and 16-deep k-step: lane l's 16 bytes are the
 // eight k of expert l%32 at k offset 8*(l/32)), so every operand load is one
-// contiguous 1 KB LDS-DMA.  route_kernel: a 256-thread workgroup owns 64
-// tokens and all E <= 128 experts; wave w computes the 64 x 32 logit block of
+// contiguous 1 KB LDS-DMA.  route_kernel: a 256-thread workgroup owns TB
+// tokens and all E <= 128 experts; wave w computes the TB x 32 logit block of
 // experts 32w.., with x tiles (K-contiguous, swizzled) and weight fragments
-// streamed into a 5-stage LDS ring.
+// streamed into an LDS ring (64 tokens: 5 stages of 32 h; 32 tokens: 3 of 64).
 //
 // Selection: one wave per token; lane l owns experts l and l+64.  Keys
 // v = s + b are turned into order-preserving 32-bit codes (NaN -> -inf) and
@@ -37,7 +37,13 @@ namespace router {
 
 using namespace lds;
 
-constexpr int NT = 256, NW = 4, TB = 64, BK = 32, STAGES = 5, EMAX = 128, EBMAX = EMAX / 32;
+#ifndef MOE_ROUTE_TB
+#define MOE_ROUTE_TB 32
+#endif
+constexpr int NT = 256, NW = 4, EMAX = 128, EBMAX = EMAX / 32;
+constexpr int TB = MOE_ROUTE_TB;                              // tokens per workgroup
+constexpr int BK = TB == 64 ? 32 : 64, STAGES = TB == 64 ? 5 : 3;
+constexpr int TM = TB / 32;                                   // 32-token blocks per wave
 constexpr int KK = BK / 16;                                   // k-steps per stage
 constexpr int A_BYTES = TB * BK * 2;                          // x tile
 constexpr int B_REGIONS = 3 * EBMAX * KK;                     // weight fragments per stage
@@ -46,7 +52,7 @@ constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 constexpr int A_PER = KcLoad<TB, BK, NW>::PER;                // x regions per wave
 constexpr int B_PER = B_REGIONS / NW;                         // weight regions per wave
 constexpr int LOADS = A_PER + B_PER;
-constexpr int SUM_BLOCK = 16;                                 // stages per partial sum
+constexpr int SUM_BLOCK = 512 / BK;                           // stages per partial sum (512 h)
 static_assert(B_REGIONS % NW == 0, "weight regions per wave");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(TB * (EMAX + 1) * 4 <= LDS_BYTES, "logit tile fits the ring");
@@ -140,9 +146,9 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
     }
   };
 
-  f32x16 acc[2], tot[2];
+  f32x16 acc[TM], tot[TM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = tot[i][r] = 0.f;
   const bool active = wave < EB;
@@ -157,11 +163,11 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
     const uint8_t* As = smem + (kt % STAGES) * STAGE_BYTES;
     const uint8_t* Bs = As + A_BYTES;
     if (active) {
-      bf16x8 af[KK][2], bq[KK][3];
+      bf16x8 af[KK][TM], bq[KK][3];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[kk][i] = frag_kc<BK>(As, 32 * i, kk, lane);
+        for (int i = 0; i < TM; ++i) af[kk][i] = frag_kc<BK>(As, 32 * i, kk, lane);
 #pragma unroll
         for (int p = 0; p < 3; ++p)
           bq[kk][p] = *(const bf16x8*)(Bs + ((p * EBMAX + wave) * KK + kk) * 1024 + lane * 16);
@@ -171,12 +177,12 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < TM; ++i)
             acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk][p], af[kk][i], acc[i], 0, 0, 0);
     }
     if ((kt % SUM_BLOCK) == SUM_BLOCK - 1 || kt + 1 == nk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           tot[i][r] += acc[i][r];
@@ -193,7 +199,7 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
   constexpr int LP = EMAX + 1;
   if (active) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         lg[(32 * i + (lane & 31)) * LP + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] =
