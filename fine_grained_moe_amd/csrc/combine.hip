@@ -13,6 +13,11 @@ namespace moe {
 namespace comb {
 
 constexpr int NT = 256, TPB = NT / 64;  // tokens per workgroup (one per wave)
+// threads per token in combine and un-permute-add (64: one wave; 256: the
+// whole workgroup streams longer stretches of each row)
+#ifndef MOE_ROW_TPT
+#define MOE_ROW_TPT 256
+#endif
 
 __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
 #pragma unroll
@@ -29,15 +34,15 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // Every k-loop below is unrolled to KMAX with k < K guards, so a lane's K row
 // loads of one chunk are all in flight together; KMAX = 8 when K <= 8 keeps
 // the register count (and so the occupancy) of the common case low.
-template <int KMAX>
+template <int KMAX, int TPT>
 __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
                                                      const uint16_t* __restrict__ y_rows,
                                                      const int32_t* __restrict__ row_of,
                                                      const float* __restrict__ topk_w,
                                                      const uint16_t* __restrict__ y_shared,
                                                      uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
+  const int lane = threadIdx.x % TPT;
+  const int t = blockIdx.x * (NT / TPT) + threadIdx.x / TPT;
   if (t >= T) return;
   int rows[KMAX];
   float g[KMAX];
@@ -47,7 +52,7 @@ __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
     g[k] = k < K ? topk_w[(int64_t)t * K + k] : 0.f;
   }
   const int nchunk = H / 8;
-  for (int c = lane; c < nchunk; c += 64) {
+  for (int c = lane; c < nchunk; c += TPT) {
     u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
     if (y_shared) vs = ((const u32x4*)(y_shared + (int64_t)t * H))[c];
 #pragma unroll
@@ -119,21 +124,21 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(int T, int H, int K,
   }
 }
 
-template <int KMAX>
+template <int KMAX, int TPT>
 __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
                                                            const uint16_t* __restrict__ dx_rows,
                                                            const int32_t* __restrict__ row_of,
                                                            const uint16_t* __restrict__ dx_shared,
                                                            const float* __restrict__ dx_router,
                                                            uint16_t* __restrict__ dx) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * TPB + (threadIdx.x >> 6);
+  const int lane = threadIdx.x % TPT;
+  const int t = blockIdx.x * (NT / TPT) + threadIdx.x / TPT;
   if (t >= T) return;
   int rows[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) rows[k] = k < K ? row_of[(int64_t)t * K + k] : 0;
   const int nchunk = H / 8;
-  for (int c = lane; c < nchunk; c += 64) {
+  for (int c = lane; c < nchunk; c += TPT) {
     u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -296,13 +301,14 @@ __global__ void __launch_bounds__(256) route_bwd_wgrad_kernel(int H, int E,
 hipError_t launch_combine(int T, int H, int K, const uint16_t* y_rows, const int32_t* row_of,
                           const float* topk_w, const uint16_t* y_shared, uint16_t* y,
                           hipStream_t s) {
-  const dim3 grid((T + comb::TPB - 1) / comb::TPB);
+  constexpr int TPT = MOE_ROW_TPT, TPB = comb::NT / TPT;
+  const dim3 grid((T + TPB - 1) / TPB);
   if (K <= 8)
-    hipLaunchKernelGGL(comb::combine_kernel<8>, grid, dim3(comb::NT), 0, s, T, H, K, y_rows, row_of,
-                       topk_w, y_shared, y);
+    hipLaunchKernelGGL((comb::combine_kernel<8, TPT>), grid, dim3(comb::NT), 0, s, T, H, K, y_rows,
+                       row_of, topk_w, y_shared, y);
   else
-    hipLaunchKernelGGL(comb::combine_kernel<16>, grid, dim3(comb::NT), 0, s, T, H, K, y_rows, row_of,
-                       topk_w, y_shared, y);
+    hipLaunchKernelGGL((comb::combine_kernel<16, TPT>), grid, dim3(comb::NT), 0, s, T, H, K, y_rows,
+                       row_of, topk_w, y_shared, y);
   return hipGetLastError();
 }
 
@@ -322,13 +328,14 @@ hipError_t launch_combine_bwd(int T, int H, int K, const uint16_t* dy, const uin
 hipError_t launch_unpermute_add(int T, int H, int K, const uint16_t* dx_rows,
                                 const int32_t* row_of, const uint16_t* dx_shared,
                                 const float* dx_router, uint16_t* dx, hipStream_t s) {
-  const dim3 grid((T + comb::TPB - 1) / comb::TPB);
+  constexpr int TPT = MOE_ROW_TPT, TPB = comb::NT / TPT;
+  const dim3 grid((T + TPB - 1) / TPB);
   if (K <= 8)
-    hipLaunchKernelGGL(comb::unpermute_add_kernel<8>, grid, dim3(comb::NT), 0, s, T, H, K, dx_rows,
-                       row_of, dx_shared, dx_router, dx);
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<8, TPT>), grid, dim3(comb::NT), 0, s, T, H, K,
+                       dx_rows, row_of, dx_shared, dx_router, dx);
   else
-    hipLaunchKernelGGL(comb::unpermute_add_kernel<16>, grid, dim3(comb::NT), 0, s, T, H, K, dx_rows,
-                       row_of, dx_shared, dx_router, dx);
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<16, TPT>), grid, dim3(comb::NT), 0, s, T, H, K,
+                       dx_rows, row_of, dx_shared, dx_router, dx);
   return hipGetLastError();
 }
 

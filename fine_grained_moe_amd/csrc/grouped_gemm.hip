@@ -94,29 +94,17 @@ struct TileCfg {
 // 64-deep k stages (128-byte row segments per load)
 using CfgRows =
     TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, MOE_ROWS_WGM, MOE_ROWS_WGN, MOE_ROWS_MINB>;
-// row tiles for the products whose columns are the hidden size H (down
-// forward, gate/up data gradient): 0 = CfgRows, 1 = 128 x 512 tiles of 8 waves
-// (wave tile 64 x 128), two 64-deep stages
-#ifndef MOE_ROWS_H
-#define MOE_ROWS_H 0
-#endif
-using CfgRowsH = std::conditional_t<MOE_ROWS_H != 0, TileCfg<128, 512, 64, 2, 2, 4, 1>, CfgRows>;
 // 256 x 256 tiles of 8 waves (wave tile 128 x 64), one workgroup per CU
 using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4, 1>;
-// tile of the K-grouped weight-gradient products: 0 = CfgWide, 1 = CfgRows
-#ifndef MOE_WGRAD_ROWS
-#define MOE_WGRAD_ROWS 0
-#endif
-using CfgWgrad = std::conditional_t<MOE_WGRAD_ROWS != 0, CfgRows, CfgWide>;
+// K-grouped weight-gradient products use the wide tile
+using CfgWgrad = CfgWide;
 static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
 
 constexpr int GROUP_M = 4;  // m-tiles per rasterization group (row-grouped, non-expert-major)
 // K-grouped weight gradients: m-tiles per rasterization group inside one
-// expert (0 = all of them, so each column slab of the second operand is used
-// by every m-tile while it is resident in L2)
-#ifndef MOE_KGROUP_GM
-#define MOE_KGROUP_GM 4
-#endif
+// expert, so a column slab of the second operand is reused by several m-tiles
+// while it is resident in L2
+constexpr int KGROUP_GM = 4;
 
 enum Src { KC = 0, MC = 1 };
 enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2 };
@@ -244,7 +232,7 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
     const int per_e = (MODE == KGROUP) ? a.n_mtiles * a.n_ntiles : 0x7fffffff;
     e = (MODE == KGROUP) ? L / per_e : 0;
     const int rem = (MODE == KGROUP) ? L % per_e : L;
-    const int GM = (MODE == KGROUP) ? (MOE_KGROUP_GM > 0 ? MOE_KGROUP_GM : n_mt) : GROUP_M;
+    const int GM = (MODE == KGROUP) ? KGROUP_GM : GROUP_M;
     const int per_group = GM * a.n_ntiles;
     const int grp = rem / per_group, within = rem % per_group;
     const int gm = min(GM, n_mt - grp * GM);
@@ -722,7 +710,7 @@ hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* 
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = F; a.F = F;
   a.lda = F; a.ldb = F; a.ldc = H; a.strideB = (int64_t)H * F; a.G = G;
-  return launch_rows<KC, KC, EPI_STORE, CfgRowsH>(a, CfgRowsH::BN, CfgWide::BN, H, s);
+  return launch_rows<KC, KC, EPI_STORE, CfgRows>(a, CfgRows::BN, CfgWide::BN, H, s);
 }
 
 hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
@@ -746,7 +734,7 @@ hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.offsets = offsets; a.counts = counts; a.tile_expert = tile_expert;
   a.m_rows = m_rows; a.N = H; a.K = 2 * F; a.F = F;
   a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = (int64_t)2 * F * H; a.G = G;
-  return launch_rows<KC, MC, EPI_STORE, CfgRowsH>(a, CfgRowsH::BN, CfgWide::BN, H, s);
+  return launch_rows<KC, MC, EPI_STORE, CfgRows>(a, CfgRows::BN, CfgWide::BN, H, s);
 }
 
 // dW2[g] [H,F] = dy_rows_g^T [H, rows] . h_g [rows, F]
