@@ -41,6 +41,19 @@ function that takes it):
   R9  no capacity limit: every token keeps all K of its experts.
   R10 experts have no linear biases; gate is the first F rows of W1, and the
       hidden activation is silu(gate) * up.
+  R11 bias update (the auxiliary-loss-free balancing step; the pages name
+      DeepSeek's bias-update trick but give neither rule nor rate): DeepSeek's
+      published sign rule, bias[e] += gamma * sign(mean load - load[e]) over
+      the per-expert token counts of a batch; an expert exactly at the mean
+      keeps its bias.
+  R12 sequence-wise balance loss (named on the pages as the complement of the
+      bias update, not defined there): DeepSeek-V3's complementary
+      sequence-wise auxiliary loss.  For a sequence of L tokens,
+      s'[t,i] = s[t,i] / sum_j s[t,j] over all E experts, P_i = mean_t s'[t,i],
+      f_i = E / (K L) * #{t : i selected by t}, loss = alpha * sum_i f_i P_i.
+      A batch of T = B L tokens holds B consecutive sequences; its loss is the
+      mean over them.  The selection is held fixed in the gradient (R7), so
+      the loss reaches the logits through all E scores of each token.
 
 Precision: products and sums in fp64; values that the method defines as fp32
 (logit, score, key, combine weight) are rounded to fp32 where they are
@@ -347,6 +360,69 @@ def unpermute_add(dx_rows, row_of, extra=()):
     for e in extra:
         dx += np.asarray(e, F64)
     return dx
+
+
+def router_bwd_dense(x, w_router, dlogit):
+    """Router gradients of a dense logit gradient dlogit [T, E] (fp64):
+    dW_r = x^T dlogit ([H, E]) and dx_r = dlogit W_r^T ([T, H])."""
+    dl = np.asarray(dlogit, F64)
+    return np.asarray(x, F64).T @ dl, dl @ np.asarray(w_router, F64).T
+
+
+# ---------------------------------------------------------------------------
+# Load balancing ([TR] "Method": DeepSeek's auxiliary-loss-free bias update,
+# complemented by a sequence-wise balance loss; [CARD] "Model Architecture
+# Features": load balancing through dynamic bias terms)
+# ---------------------------------------------------------------------------
+def bias_update(bias, counts, gamma):
+    """One bias step from a batch's per-expert token counts (R11).
+
+    An expert's load is compared with the mean load sum(counts)/E exactly, in
+    integers (E * count against the total); the bias moves by gamma towards
+    balance in one fp32 addition.  Returns the new fp32 bias.
+    """
+    c = np.asarray(counts, np.int64)
+    E = c.shape[0]
+    direction = np.sign(c.sum() - E * c).astype(F32)  # +1 below the mean, -1 above
+    return (np.asarray(bias, F32) + direction * F32(gamma)).astype(F32)
+
+
+def seq_balance_stats(scores, topk_idx, seq_len):
+    """Per-sequence f [B, E] and P [B, E] of the sequence-wise balance loss (R12)."""
+    s = np.asarray(scores, F64)
+    T, E = s.shape
+    K = topk_idx.shape[1]
+    B = T // seq_len
+    s_norm = s / s.sum(axis=1, keepdims=True)
+    P = s_norm.reshape(B, seq_len, E).mean(axis=1)
+    picked = np.zeros((T, E), F64)
+    np.put_along_axis(picked, topk_idx.astype(np.int64), 1.0, axis=1)
+    f = picked.reshape(B, seq_len, E).sum(axis=1) * (E / (K * seq_len))
+    return f, P
+
+
+def seq_balance_loss(scores, topk_idx, seq_len, alpha):
+    """loss = mean over the B sequences of alpha * sum_i f_i P_i (R12); fp64."""
+    f, P = seq_balance_stats(scores, topk_idx, seq_len)
+    return float(alpha * (f * P).sum(axis=1).mean())
+
+
+def seq_balance_bwd(scores, topk_idx, seq_len, alpha, dloss=1.0):
+    """Gradient of dloss * loss with respect to the logits, dense [T, E] (fp64).
+
+    With c_i = dloss * alpha * f_i / (B L) for the token's sequence,
+    dL/ds'[t,i] = c_i; through s' = s / sum(s):
+      ds[t,j]     = (c_j - sum_i c_i s'[t,i]) / sum_i s[t,i]
+    and through s = sigmoid(logit): dlogit = ds * s * (1 - s).
+    """
+    s = np.asarray(scores, F64)
+    T, E = s.shape
+    B = T // seq_len
+    f, _ = seq_balance_stats(scores, topk_idx, seq_len)
+    c = np.repeat(f * (dloss * alpha / (B * seq_len)), seq_len, axis=0)
+    tot = s.sum(axis=1, keepdims=True)
+    ds = (c - (c * (s / tot)).sum(axis=1, keepdims=True)) / tot
+    return ds * s * (1.0 - s)
 
 
 # ---------------------------------------------------------------------------

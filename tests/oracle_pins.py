@@ -14,6 +14,10 @@ Pins used:
   * closed forms and invariants: sigmoid values, sum of combine weights,
     routing independence when all experts are identical, central finite
     differences of the forward.
+  * load balancing: hand-worked bias steps and balance losses, the loss's
+    closed forms (uniform scores or balanced picks give alpha, collapsed
+    routing gives alpha E / K), the bias rule driving a skewed router towards
+    balance, and central finite differences of the loss in the logits.
 """
 from __future__ import annotations
 
@@ -394,3 +398,148 @@ def check_backward_finite_differences(O, inp, K, align, n_coords=12, seed=5):
             fd = (lp - lm) / (2 * h)
             scale = max(1.0, float(np.abs(grad).max()))
             assert abs(fd - grad[idx]) <= 1e-5 * scale, (name, idx, fd, grad[idx])
+
+
+# ---------------------------------------------------------------------------
+# Load balancing
+# ---------------------------------------------------------------------------
+def check_bias_update_golden(O):
+    for c in load_golden("balance_small.json")["bias_update"]:
+        got = O.bias_update(np.array(c["bias"], np.float32), np.array(c["counts"], np.int32),
+                            c["gamma"])
+        assert got.dtype == np.float32
+        assert np.array_equal(got, np.array(c["new_bias"], np.float32)), (c["name"], got)
+
+
+def check_bias_update_invariants(O, seed=7):
+    """Each bias moves by exactly +-gamma (to fp32 rounding) or not at all,
+    against the sign of its load's excess over the mean (computed in fp64)."""
+    rng = np.random.default_rng(seed)
+    for E in (1, 2, 8, 128):
+        counts = rng.integers(0, 50, E)
+        if E > 2:
+            counts[0] = counts[1:].sum() // (E - 1)  # some experts near the mean
+        bias = rng.standard_normal(E).astype(np.float32)
+        gamma = np.float32(1e-3)
+        new = O.bias_update(bias, counts, gamma)
+        step = new.astype(np.float64) - bias.astype(np.float64)
+        excess = counts - counts.sum() / E
+        for e in range(E):
+            if excess[e] == 0:
+                assert step[e] == 0.0
+            else:
+                assert -np.sign(excess[e]) * step[e] > 0.5 * gamma
+                assert abs(abs(step[e]) - gamma) <= 1e-6 * max(1.0, abs(bias[e]))
+
+
+def check_bias_update_balances_router(O, steps=60):
+    """The rule's purpose: on a router whose bias strongly favours a few
+    experts, repeated (route, count, update) steps spread the load."""
+    rng = np.random.default_rng(21)
+    T, H, E, K = 256, 16, 8, 2
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w = (rng.standard_normal((H, E)) * 0.1).astype(np.float32)
+    bias = np.linspace(0.4, -0.4, E).astype(np.float32)
+
+    def imbalance(b):
+        idx = O.route(x, w, b, K)["topk_idx"]
+        counts = np.bincount(idx.ravel(), minlength=E)
+        return counts, counts.max() / (T * K / E)
+
+    counts, start = imbalance(bias)
+    for _ in range(steps):
+        bias = O.bias_update(bias, counts, 0.02)
+        counts, now = imbalance(bias)
+    assert start > 3.0 and now < 1.5, (start, now)
+
+
+def seq_loss_bruteforce(scores, topk_idx, seq_len, alpha):
+    """Plain loops: per sequence and expert, the fraction of picks scaled by
+    E/K, times the mean normalised score; averaged over sequences."""
+    T, E = len(scores), len(scores[0])
+    K = len(topk_idx[0])
+    per_seq = []
+    for b in range(T // seq_len):
+        toks = range(b * seq_len, (b + 1) * seq_len)
+        total = []
+        for i in range(E):
+            picks = sum(1 for t in toks if i in list(topk_idx[t]))
+            f = E * picks / (K * seq_len)
+            P = math.fsum(scores[t][i] / math.fsum(scores[t]) for t in toks) / seq_len
+            total.append(f * P)
+        per_seq.append(alpha * math.fsum(total))
+    return math.fsum(per_seq) / len(per_seq)
+
+
+def check_seq_loss_golden(O):
+    for c in load_golden("balance_small.json")["seq_loss"]:
+        got = O.seq_balance_loss(np.array(c["scores"], np.float32),
+                                 np.array(c["topk_idx"], np.int32), c["seq_len"], c["alpha"])
+        assert abs(got - c["loss"]) <= 1e-6 * abs(c["loss"]), (c["name"], got)
+
+
+def check_seq_loss_closed_forms(O, seed=9):
+    rng = np.random.default_rng(seed)
+    T, E, K, L, alpha = 24, 8, 2, 6, 0.3
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    s = rng.uniform(0.05, 0.95, (T, E)).astype(np.float32)
+    # every expert scored alike: P_i = 1/E, sum_i f_i = E, loss = alpha
+    flat = np.full((T, E), 0.37, np.float32)
+    assert abs(O.seq_balance_loss(flat, idx, L, alpha) - alpha) < 1e-9
+    # every sequence picks each expert equally often: f_i = 1, loss = alpha
+    bal = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)], np.int32)
+    assert abs(O.seq_balance_loss(s, bal, 4, alpha) - alpha) < 1e-9
+    # collapsed: all tokens pick experts 0..K-1 and score only them
+    col = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    sc = np.zeros((T, E), np.float32)
+    sc[:, :K] = 0.6
+    assert abs(O.seq_balance_loss(sc, col, L, alpha) - alpha * E / K) < 1e-9
+    # plain-loop evaluation on random scores and picks
+    ref = seq_loss_bruteforce(s.astype(np.float64).tolist(), idx.tolist(), L, alpha)
+    assert abs(O.seq_balance_loss(s, idx, L, alpha) - ref) <= 1e-12 * abs(ref)
+
+
+def check_seq_loss_finite_differences(O, seed=13, n_coords=24):
+    """dlogit from seq_balance_bwd against central differences of the loss,
+    with the selection held fixed, on the fp64 scores of perturbed logits."""
+    rng = np.random.default_rng(seed)
+    T, E, K, L, alpha, dloss = 12, 6, 2, 4, 0.7, 1.3
+    logits = rng.standard_normal((T, E))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+
+    def loss(lg):
+        return dloss * O.seq_balance_loss(1.0 / (1.0 + np.exp(-lg)), idx, L, alpha)
+
+    got = O.seq_balance_bwd(1.0 / (1.0 + np.exp(-logits)), idx, L, alpha, dloss)
+    h = 1e-6
+    for _ in range(n_coords):
+        t, e = rng.integers(T), rng.integers(E)
+        p, m = logits.copy(), logits.copy()
+        p[t, e] += h
+        m[t, e] -= h
+        fd = (loss(p) - loss(m)) / (2 * h)
+        assert abs(got[t, e] - fd) <= 1e-6 * max(1e-3, abs(fd)), (t, e, got[t, e], fd)
+
+
+def check_router_bwd_dense(O, seed=17):
+    """The dense router backward reproduces the sparse one on its own
+    (sparse) logit gradient, and is the gradient of sum((x W) * dlogit)."""
+    inp, K = small_inputs(seed=seed)
+    x, w = inp["x"], inp["w_router"]
+    r = O.route(x, w, inp["bias"], K)
+    dg = np.random.default_rng(seed).standard_normal(r["topk_idx"].shape)
+    dW, dx, dl = O.router_bwd(x, w, r["topk_idx"], r["topk_s"], dg)
+    dW2, dx2 = O.router_bwd_dense(x, w, dl)
+    assert np.allclose(dW, dW2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dx, dx2, rtol=1e-12, atol=1e-12)
+    x64, w64 = x.astype(np.float64), w.astype(np.float64)
+    for (h_, e_) in ((0, 0), (3, 5), (15, 2)):
+        d = np.zeros_like(w64)
+        d[h_, e_] = 1e-3
+        fd = (np.sum((x64 @ (w64 + d)) * dl) - np.sum((x64 @ (w64 - d)) * dl)) / 2e-3
+        assert abs(dW2[h_, e_] - fd) <= 1e-9 * max(1.0, abs(fd))
+    for (t_, h_) in ((0, 0), (7, 9)):
+        d = np.zeros_like(x64)
+        d[t_, h_] = 1e-3
+        fd = (np.sum(((x64 + d) @ w64) * dl) - np.sum(((x64 - d) @ w64) * dl)) / 2e-3
+        assert abs(dx2[t_, h_] - fd) <= 1e-9 * max(1.0, abs(fd))

@@ -28,6 +28,12 @@ def _all_pins():
         lambda: P.check_one_expert_is_dense_swiglu(O),
         lambda: P.check_identical_experts_independent_of_routing(O, inp, K, 4),
         lambda: P.check_backward_autograd(O, inp, K, 4),
+        lambda: P.check_bias_update_golden(O),
+        lambda: P.check_bias_update_balances_router(O),
+        lambda: P.check_seq_loss_golden(O),
+        lambda: P.check_seq_loss_closed_forms(O),
+        lambda: P.check_seq_loss_finite_differences(O),
+        lambda: P.check_router_bwd_dense(O),
     ]
 
 
@@ -135,6 +141,45 @@ def m_dW2_transposed_rows(x_rows, w1e, w2e, a, dy_rows):
     return dx, dW1, dW2[::-1].copy(), da
 
 
+def m_bias_update_sign_flipped(bias, counts, gamma):
+    return _orig["bias_update"](bias, counts, -gamma)
+
+
+def m_bias_update_moves_at_mean(bias, counts, gamma):
+    c = np.asarray(counts, np.int64)
+    d = np.where(c * len(c) >= c.sum(), -1.0, 1.0).astype(np.float32)
+    return (np.asarray(bias, np.float32) + d * np.float32(gamma)).astype(np.float32)
+
+
+def m_seq_loss_sum_over_sequences(scores, topk_idx, seq_len, alpha):
+    B = len(scores) // seq_len
+    return B * _orig["seq_balance_loss"](scores, topk_idx, seq_len, alpha)
+
+
+def m_seq_stats_without_e_over_k(scores, topk_idx, seq_len):
+    f, P = _orig["seq_balance_stats"](scores, topk_idx, seq_len)
+    E, K = np.asarray(scores).shape[1], topk_idx.shape[1]
+    return f * K / E, P
+
+
+def m_seq_bwd_no_normalisation_term(scores, topk_idx, seq_len, alpha, dloss=1.0):
+    s = np.asarray(scores, F64)
+    B = s.shape[0] // seq_len
+    f, _ = O.seq_balance_stats(scores, topk_idx, seq_len)
+    c = np.repeat(f * (dloss * alpha / (B * seq_len)), seq_len, axis=0)
+    return c / s.sum(axis=1, keepdims=True) * s * (1.0 - s)
+
+
+def m_seq_bwd_no_sigmoid_grad(scores, topk_idx, seq_len, alpha, dloss=1.0):
+    s = np.asarray(scores, F64)
+    return _orig["seq_balance_bwd"](scores, topk_idx, seq_len, alpha, dloss) / (s * (1.0 - s))
+
+
+def m_router_bwd_dense_drops_dx(x, w_router, dlogit):
+    dW, dx = _orig["router_bwd_dense"](x, w_router, dlogit)
+    return dW, 0.5 * dx
+
+
 MUTATIONS = {
     "logits_drop_last_term": ("router_logits", m_logits_drop_last_term),
     "sigmoid_wrong_sign": ("sigmoid64", m_sigmoid_wrong_sign),
@@ -151,6 +196,13 @@ MUTATIONS = {
     "router_bwd_sign": ("router_bwd", m_router_bwd_sign),
     "router_bwd_no_dx": ("router_bwd", m_router_bwd_no_dx),
     "dW2_rows_reversed": ("expert_ffn_bwd", m_dW2_transposed_rows),
+    "bias_update_sign_flipped": ("bias_update", m_bias_update_sign_flipped),
+    "bias_update_moves_at_mean": ("bias_update", m_bias_update_moves_at_mean),
+    "seq_loss_sum_over_sequences": ("seq_balance_loss", m_seq_loss_sum_over_sequences),
+    "seq_stats_without_e_over_k": ("seq_balance_stats", m_seq_stats_without_e_over_k),
+    "seq_bwd_no_normalisation_term": ("seq_balance_bwd", m_seq_bwd_no_normalisation_term),
+    "seq_bwd_no_sigmoid_grad": ("seq_balance_bwd", m_seq_bwd_no_sigmoid_grad),
+    "router_bwd_dense_scaled_dx": ("router_bwd_dense", m_router_bwd_dense_drops_dx),
 }
 
 

@@ -150,3 +150,31 @@ def test_empty_expert_weight_gradient_is_zero(small):
     bwd = O.backward(inp, fwd, inp["dy"])
     assert (bwd["dW1"][0] == 0).all() and (bwd["dW2"][0] == 0).all()
     assert (bwd["dW_r"][:, 0] == 0).all()
+
+
+def test_bias_update_golden():
+    P.check_bias_update_golden(O)
+
+
+def test_bias_update_invariants():
+    P.check_bias_update_invariants(O)
+
+
+def test_bias_update_balances_router():
+    P.check_bias_update_balances_router(O)
+
+
+def test_seq_loss_golden():
+    P.check_seq_loss_golden(O)
+
+
+def test_seq_loss_closed_forms():
+    P.check_seq_loss_closed_forms(O)
+
+
+def test_seq_loss_finite_differences():
+    P.check_seq_loss_finite_differences(O)
+
+
+def test_router_bwd_dense():
+    P.check_router_bwd_dense(O)
