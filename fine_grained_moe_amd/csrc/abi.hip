@@ -82,9 +82,20 @@ size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K)
   return moe::route_bwd_workspace_bytes(capacity(T, E, K), H, E);
 }
 
+size_t moe_seq_balance_workspace_bytes(int32_t T, int32_t E, int32_t seq_len) {
+  if (T < 0 || E <= 0 || E > 128 || seq_len <= 0 || T % seq_len != 0) return 0;
+  return moe::seq_balance_workspace_bytes(T, E, seq_len);
+}
+
+size_t moe_route_bwd_dense_workspace_bytes(int32_t T, int32_t H, int32_t E) {
+  if (T < 0 || H <= 0 || E <= 0 || E > 128) return 0;
+  return moe::route_bwd_dense_workspace_bytes(T, H, E);
+}
+
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
                        const float* w_router, const float* bias, int32_t* topk_idx,
-                       float* topk_w, float* topk_s, void* ws, size_t ws_bytes, void* stream) {
+                       float* topk_w, float* topk_s, float* scores, void* ws, size_t ws_bytes,
+                       void* stream) {
   moe_status_t st = check_dims(__func__, T, H, E, K);
   if (st) return st;
   if (T == 0) return MOE_OK;
@@ -92,7 +103,7 @@ moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_workspace_bytes(H, E),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   return hip_status(moe::launch_route(T, H, E, K, x, w_router, bias, topk_idx, topk_w, topk_s,
-                                      ws, (hipStream_t)stream),
+                                      scores, ws, (hipStream_t)stream),
                     __func__);
 }
 
@@ -309,6 +320,66 @@ moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx
   REQUIRE(dx_rows && row_of && dx, MOE_ERR_INVALID_ARGUMENT, "null pointer");
   return hip_status(moe::launch_unpermute_add(T, H, K, dx_rows, row_of, dx_shared, dx_router, dx,
                                               (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_bias_update(int32_t E, const int32_t* counts, float* bias, float gamma,
+                             void* stream) {
+  REQUIRE(E > 0, MOE_ERR_INVALID_ARGUMENT, "E <= 0");
+  REQUIRE(E <= 128, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128");
+  REQUIRE(counts && bias, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_bias_update(E, counts, bias, gamma, (hipStream_t)stream),
+                    __func__);
+}
+
+static moe_status_t check_seq(const char* fn, int32_t T, int32_t E, int32_t K, int32_t seq_len) {
+  if (T <= 0 || E <= 0 || K <= 0 || seq_len <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, fn, "T, E, K or seq_len <= 0");
+  if (K > E) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "K > E");
+  if (T % seq_len != 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "T % seq_len != 0");
+  if (E > 128 || K > 16) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "E > 128 or K > 16");
+  if ((int64_t)T * E >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "T*E too large");
+  return MOE_OK;
+}
+
+moe_status_t moe_seq_balance_fwd(int32_t T, int32_t E, int32_t K, int32_t seq_len,
+                                 const float* scores, const int32_t* topk_idx, float alpha,
+                                 float* loss, float* seq_f, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  moe_status_t st = check_seq(__func__, T, E, K, seq_len);
+  if (st) return st;
+  REQUIRE(scores && topk_idx && loss && seq_f, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(ws != nullptr && ws_bytes >= moe_seq_balance_workspace_bytes(T, E, seq_len),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return hip_status(moe::launch_seq_balance_fwd(T, E, K, seq_len, scores, topk_idx, alpha, loss,
+                                                seq_f, ws, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_len,
+                                 const float* scores, const float* seq_f, float alpha,
+                                 const float* dloss, float* dlogit, void* stream) {
+  moe_status_t st = check_seq(__func__, T, E, K, seq_len);
+  if (st) return st;
+  REQUIRE(scores && seq_f && dlogit, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_seq_balance_bwd(T, E, seq_len, scores, seq_f, alpha, dloss,
+                                                dlogit, (hipStream_t)stream),
+                    __func__);
+}
+
+moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t* x,
+                                 const float* w_router, const float* dlogit, float* dw_router,
+                                 float* dx_router, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(T >= 0 && H > 0 && E > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,E<=0");
+  REQUIRE(E <= 128 && H % 64 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128 or H % 64 != 0");
+  REQUIRE((int64_t)T * H < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED_SHAPE, "T*H too large");
+  if (T == 0) return MOE_OK;
+  REQUIRE(x && w_router && dlogit && dw_router && dx_router, MOE_ERR_INVALID_ARGUMENT,
+          "null pointer");
+  REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_dense_workspace_bytes(T, H, E),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return hip_status(moe::launch_route_bwd_dense(T, H, E, x, w_router, dlogit, dw_router,
+                                                dx_router, ws, (hipStream_t)stream),
                     __func__);
 }
 

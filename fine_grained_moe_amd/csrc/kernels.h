@@ -11,7 +11,7 @@ constexpr int kAlign = 128;  // grouped-GEMM row tile = segment alignment
 size_t route_workspace_bytes(int H, int E);
 hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
-                        void* ws, hipStream_t s);
+                        float* scores, void* ws, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
@@ -57,5 +57,19 @@ hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x_rows,
                             const float* dg, const int32_t* row_of, const int32_t* offsets,
                             const int32_t* counts, float* dw_router, float* dx_router, void* ws,
                             hipStream_t s);
+
+
+hipError_t launch_bias_update(int E, const int32_t* counts, float* bias, float gamma,
+                              hipStream_t s);
+size_t seq_balance_workspace_bytes(int T, int E, int L);
+hipError_t launch_seq_balance_fwd(int T, int E, int K, int L, const float* scores,
+                                  const int32_t* topk_idx, float alpha, float* loss, float* seq_f,
+                                  void* ws, hipStream_t s);
+hipError_t launch_seq_balance_bwd(int T, int E, int L, const float* scores, const float* seq_f,
+                                  float alpha, const float* dloss, float* dlogit, hipStream_t s);
+size_t route_bwd_dense_workspace_bytes(int T, int H, int E);
+hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const float* w_router,
+                                  const float* dlogit, float* dw_router, float* dx_router,
+                                  void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -115,7 +115,8 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
                                                       const float* __restrict__ bias,
                                                       int32_t* __restrict__ topk_idx,
                                                       float* __restrict__ topk_w,
-                                                      float* __restrict__ topk_s) {
+                                                      float* __restrict__ topk_s,
+                                                      float* __restrict__ scores) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -219,6 +220,7 @@ __global__ void __launch_bounds__(NT, 1) route_kernel(int T, int H, int E, int K
       if (e < E) {
         const float z = lg[tt * LP + e];
         sc[q] = 1.0f / (1.0f + expf(-z));
+        if (scores) scores[(int64_t)t * E + e] = sc[q];
         const float v = sc[q] + bias[e];
         key[q] = ((uint64_t)order_code(v) << 32) | (uint32_t)(0xFFFFu - e);
       } else {
@@ -261,7 +263,7 @@ size_t route_workspace_bytes(int H, int E) {
 
 hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
-                        void* ws, hipStream_t s) {
+                        float* scores, void* ws, hipStream_t s) {
   uint16_t* wf = (uint16_t*)ws;
   hipLaunchKernelGGL(router::split_kernel, dim3(H / 16, (E + 31) / 32), dim3(64), 0, s, H, E,
                      w_router, wf);
@@ -269,7 +271,7 @@ hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const flo
   if (e != hipSuccess || T == 0) return e;
   const int nb = (T + router::TB - 1) / router::TB;
   hipLaunchKernelGGL(router::route_kernel, dim3(nb), dim3(router::NT), 0, s, T, H, E, K, x, wf,
-                     bias, topk_idx, topk_w, topk_s);
+                     bias, topk_idx, topk_w, topk_s, scores);
   return hipGetLastError();
 }
 

@@ -30,7 +30,9 @@ _SIGS = {
     "moe_route_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
-    "moe_route": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_seq_balance_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route_bwd_dense_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_permute": (_i32, [_i32, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
                            _p, _sz, _p]),
     "moe_grouped_swiglu_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -48,6 +50,11 @@ _SIGS = {
     "moe_route_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                              _sz, _p]),
     "moe_permute_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "moe_bias_update": (_i32, [_i32, _p, _p, ctypes.c_float, _p]),
+    "moe_seq_balance_fwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p, _sz,
+                                   _p]),
+    "moe_seq_balance_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p]),
+    "moe_route_bwd_dense": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -113,7 +120,18 @@ def moe_route_bwd_workspace_bytes(T: int, H: int, E: int, K: int) -> int:
 # ---------------------------------------------------------------------------
 # entry points (outputs allocated when not given)
 # ---------------------------------------------------------------------------
-def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=None):
+def moe_seq_balance_workspace_bytes(T: int, E: int, seq_len: int) -> int:
+    return int(_lib.moe_seq_balance_workspace_bytes(T, E, seq_len))
+
+
+def moe_route_bwd_dense_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(_lib.moe_route_bwd_dense_workspace_bytes(T, H, E))
+
+
+def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=None,
+              scores=None):
+    """Returns (topk_idx, topk_w, topk_s); pass a [T,E] fp32 `scores` tensor to
+    also receive every expert's score."""
     T, H = x.shape
     E = w_router.shape[1]
     dev = x.device
@@ -125,7 +143,7 @@ def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=
     _check(_lib.moe_route(T, H, E, K, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                           _ptr(bias, F32, "bias"), _ptr(topk_idx, I32, "topk_idx"),
                           _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"),
-                          _ptr(ws), ws.numel(), _stream()))
+                          _ptr(scores, F32, "scores"), _ptr(ws), ws.numel(), _stream()))
     return topk_idx, topk_w, topk_s
 
 
@@ -331,6 +349,58 @@ def moe_permute_bwd(dx_rows, row_of, dx_shared=None, dx_router=None, dx=None):
     return dx
 
 
+def moe_bias_update(counts, bias, gamma):
+    """Updates bias (fp32 [E], in place) from the per-expert counts; returns bias."""
+    E = bias.shape[0]
+    _check(_lib.moe_bias_update(E, _ptr(counts, I32, "counts"), _ptr(bias, F32, "bias"),
+                                float(gamma), _stream()))
+    return bias
+
+
+def moe_seq_balance_fwd(scores, topk_idx, seq_len, alpha, loss=None, seq_f=None, ws=None):
+    """Returns (loss [1] fp32, seq_f [T/seq_len, E] fp32)."""
+    T, E = scores.shape
+    K = topk_idx.shape[1]
+    dev = scores.device
+    loss = torch.empty(1, dtype=F32, device=dev) if loss is None else loss
+    B = T // seq_len if seq_len > 0 else 0
+    seq_f = torch.empty((max(B, 1), E), dtype=F32, device=dev) if seq_f is None else seq_f
+    if ws is None:
+        ws = torch.empty(max(moe_seq_balance_workspace_bytes(T, E, seq_len), 1), dtype=torch.uint8,
+                         device=dev)
+    _check(_lib.moe_seq_balance_fwd(T, E, K, seq_len, _ptr(scores, F32, "scores"),
+                                    _ptr(topk_idx, I32, "topk_idx"), float(alpha),
+                                    _ptr(loss, F32, "loss"), _ptr(seq_f, F32, "seq_f"), _ptr(ws),
+                                    ws.numel(), _stream()))
+    return loss, seq_f
+
+
+def moe_seq_balance_bwd(scores, seq_f, K, seq_len, alpha, dloss=None, dlogit=None):
+    """Returns dlogit [T,E] fp32 (dloss: fp32 [1] device tensor or None for 1)."""
+    T, E = scores.shape
+    dlogit = torch.empty((T, E), dtype=F32, device=scores.device) if dlogit is None else dlogit
+    _check(_lib.moe_seq_balance_bwd(T, E, K, seq_len, _ptr(scores, F32, "scores"),
+                                    _ptr(seq_f, F32, "seq_f"), float(alpha),
+                                    _ptr(dloss, F32, "dloss"), _ptr(dlogit, F32, "dlogit"),
+                                    _stream()))
+    return dlogit
+
+
+def moe_route_bwd_dense(x, w_router, dlogit, dw_router, dx_router, ws=None):
+    """Adds the router gradients of a dense dlogit [T,E] into dw_router [H,E]
+    and dx_router [T,H] (both fp32, updated in place)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    if ws is None:
+        ws = torch.empty(max(moe_route_bwd_dense_workspace_bytes(T, H, E), 1), dtype=torch.uint8,
+                         device=x.device)
+    _check(_lib.moe_route_bwd_dense(T, H, E, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
+                                    _ptr(dlogit, F32, "dlogit"), _ptr(dw_router, F32, "dw_router"),
+                                    _ptr(dx_router, F32, "dx_router"), _ptr(ws), ws.numel(),
+                                    _stream()))
+    return dw_router, dx_router
+
+
 # ---------------------------------------------------------------------------
 # the whole layer, composed from the entry points above
 # ---------------------------------------------------------------------------
@@ -345,11 +415,15 @@ def fuse_shared(w1_sh, w2_sh):
     return w1f.unsqueeze(0).contiguous(), w2f.unsqueeze(0).contiguous()
 
 
-def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backward=True):
+def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backward=True,
+                  balance=None):
     """Forward of the MoE layer.  w1_shf / w2_shf are the fused shared weights
-    (fuse_shared), or None for no shared experts.  Returns (y, ctx)."""
+    (fuse_shared), or None for no shared experts.  balance = (alpha, seq_len)
+    adds the sequence-wise balance loss (ctx["balance_loss"]).  Returns (y, ctx)."""
     E = w1.shape[0]
-    topk_idx, topk_w, topk_s = moe_route(x, w_router, bias, K)
+    T = x.shape[0]
+    scores = None if balance is None else torch.empty((T, E), dtype=F32, device=x.device)
+    topk_idx, topk_w, topk_s = moe_route(x, w_router, bias, K, scores=scores)
     p = moe_permute(topk_idx, x, E)
     act, h, y_rows = moe_grouped_swiglu_fwd(p["x_rows"], w1, w2, p["offsets"], p["counts"],
                                             p["tile_expert"], act=save_for_backward)
@@ -359,13 +433,18 @@ def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backwar
     y = moe_combine(y_rows, p["row_of"], topk_w, y_sh)
     ctx = dict(x=x, w_router=w_router, w1=w1, w2=w2, w1_shf=w1_shf, w2_shf=w2_shf,
                topk_idx=topk_idx, topk_w=topk_w, topk_s=topk_s, perm=p, act=act, h=h,
-               y_rows=y_rows, y_sh=y_sh, act_sh=act_sh, h_sh=h_sh)
+               y_rows=y_rows, y_sh=y_sh, act_sh=act_sh, h_sh=h_sh, balance=balance)
+    if balance is not None:
+        alpha, seq_len = balance
+        ctx["scores"] = scores
+        ctx["balance_loss"], ctx["seq_f"] = moe_seq_balance_fwd(scores, topk_idx, seq_len, alpha)
     return y, ctx
 
 
-def layer_backward(dy, ctx):
-    """Backward of the MoE layer.  Returns dict(dx, dw1, dw2, dw1_sh, dw2_sh,
-    dw_router) plus the intermediates."""
+def layer_backward(dy, ctx, dloss=None):
+    """Backward of the MoE layer (dloss: upstream gradient of the balance
+    loss, fp32 [1] device tensor, None = 1).  Returns dict(dx, dw1, dw2,
+    dw1_sh, dw2_sh, dw_router) plus the intermediates."""
     p = ctx["perm"]
     dy_rows, dg = moe_combine_bwd(dy, ctx["y_rows"], p["row_of"], ctx["topk_w"])
     dact, dx_rows, dw1, dw2 = moe_grouped_swiglu_bwd(p["x_rows"], ctx["w1"], ctx["w2"], ctx["act"],
@@ -377,7 +456,13 @@ def layer_backward(dy, ctx):
                                                           ctx["act_sh"], ctx["h_sh"], dy)
     dw_router, dx_router = moe_route_bwd(p["x_rows"], ctx["w_router"], ctx["topk_idx"],
                                          ctx["topk_s"], dg, p["row_of"], p["offsets"], p["counts"])
+    dlogit_bal = None
+    if ctx.get("balance") is not None:
+        alpha, seq_len = ctx["balance"]
+        dlogit_bal = moe_seq_balance_bwd(ctx["scores"], ctx["seq_f"], ctx["topk_idx"].shape[1],
+                                         seq_len, alpha, dloss)
+        moe_route_bwd_dense(ctx["x"], ctx["w_router"], dlogit_bal, dw_router, dx_router)
     dx = moe_permute_bwd(dx_rows, p["row_of"], dx_sh, dx_router)
     return dict(dx=dx, dw1=dw1, dw2=dw2, dw1_sh=dw1_sh, dw2_sh=dw2_sh, dw_router=dw_router,
                 dg=dg, dy_rows=dy_rows, dact=dact, dx_rows=dx_rows, dx_shared=dx_sh,
-                dx_router=dx_router)
+                dx_router=dx_router, dlogit_balance=dlogit_bal)

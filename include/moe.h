@@ -79,6 +79,13 @@ size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
 /* host: bytes of the workspace moe_route_bwd needs. */
 size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K);
 
+/* host: bytes of the workspace moe_seq_balance_fwd needs (0 for invalid
+ * arguments, including T % seq_len != 0). */
+size_t moe_seq_balance_workspace_bytes(int32_t T, int32_t E, int32_t seq_len);
+
+/* host: bytes of the workspace moe_route_bwd_dense needs. */
+size_t moe_route_bwd_dense_workspace_bytes(int32_t T, int32_t H, int32_t E);
+
 /*
  * moe_route - FP32 gating, selection bias, top-K, combine weights.
  * (Technical Report summary, "Method": gating projection in FP32, top-6 of 128,
@@ -93,13 +100,15 @@ size_t moe_route_bwd_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t K)
  *   topk_w[t,k]   = topk_s[t,k] / sum_j topk_s[t,j]
  *
  * x [T,H] bf16; w_router [H,E] fp32; bias [E] fp32;
- * topk_idx [T,K] int32; topk_w [T,K] fp32; topk_s [T,K] fp32 (nullable).
+ * topk_idx [T,K] int32; topk_w [T,K] fp32; topk_s [T,K] fp32 (nullable);
+ * scores [T,E] fp32 (nullable): every s[t,e], the input of the sequence-wise
+ * balance loss (moe_seq_balance_fwd / _bwd).
  * ws: device workspace of at least moe_route_workspace_bytes(H,E) bytes (the
  * router weight re-encoded for the matrix cores; rewritten by every call).
  */
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K,
                        const uint16_t* x, const float* w_router, const float* bias,
-                       int32_t* topk_idx, float* topk_w, float* topk_s,
+                       int32_t* topk_idx, float* topk_w, float* topk_s, float* scores,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -279,6 +288,70 @@ moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K,
 moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx_rows,
                              const int32_t* row_of, const uint16_t* dx_shared,
                              const float* dx_router, uint16_t* dx, void* stream);
+
+/*
+ * Load balancing.  Technical Report summary, "Method": balancing by DeepSeek's
+ * auxiliary-loss-free bias update, complemented by a sequence-wise balance
+ * loss; model card, "Model Architecture Features": dynamic bias terms.  The
+ * pages define neither; the entry points below take DeepSeek's published
+ * forms.
+ */
+
+/*
+ * moe_bias_update - one auxiliary-loss-free bias step from a batch's loads:
+ *   bias[e] += gamma * sign(sum_j counts[j] / E - counts[e])
+ * An expert above the mean load has its bias lowered by gamma, one below it
+ * raised, one exactly at the mean unchanged; the comparison is exact (integer
+ * E * counts[e] against the total) and the update is one fp32 addition.
+ * counts [E] int32 (moe_permute's counts, or the caller's sum of them over
+ * micro-batches or ranks); bias [E] fp32, updated in place; gamma (host) is
+ * the step.  E <= 128.
+ */
+moe_status_t moe_bias_update(int32_t E, const int32_t* counts, float* bias, float gamma,
+                             void* stream);
+
+/*
+ * moe_seq_balance_fwd - sequence-wise balance loss.  The T tokens are B =
+ * T / seq_len consecutive sequences of seq_len tokens.  For sequence b:
+ *   s'[t,i]  = scores[t,i] / sum_j scores[t,j]          (all E experts)
+ *   P[b,i]   = mean over the sequence's tokens of s'[t,i]
+ *   f[b,i]   = E / (K seq_len) * (number of its tokens with i in topk_idx[t,:])
+ *   loss_b   = alpha * sum_i f[b,i] P[b,i]
+ *   loss[0]  = mean over b of loss_b                     (fp32, device)
+ * scores [T,E] fp32 from moe_route; topk_idx [T,K]; seq_f [B,E] fp32 receives
+ * f, which moe_seq_balance_bwd takes.  ws: at least
+ * moe_seq_balance_workspace_bytes(T,E,seq_len) bytes.  T % seq_len must be 0.
+ */
+moe_status_t moe_seq_balance_fwd(int32_t T, int32_t E, int32_t K, int32_t seq_len,
+                                 const float* scores, const int32_t* topk_idx, float alpha,
+                                 float* loss, float* seq_f, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * moe_seq_balance_bwd - gradient of dloss * loss with respect to the logits,
+ * with the selection (and so f) held fixed.  For token t of sequence b, with
+ * c_i = dloss * alpha * f[b,i] / (B seq_len) and S = sum_i scores[t,i]:
+ *   dlogit[t,e] = (c_e - sum_i c_i scores[t,i] / S) / S * s (1 - s),
+ *   s = scores[t,e]                                     (fp32 [T,E], written)
+ * dloss: device pointer to the upstream gradient of loss[0] (NULL = 1).
+ * The result is dense over all E experts; moe_route_bwd_dense turns it into
+ * router-weight and input gradients.
+ */
+moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_len,
+                                 const float* scores, const float* seq_f, float alpha,
+                                 const float* dloss, float* dlogit, void* stream);
+
+/*
+ * moe_route_bwd_dense - router gradients of a dense logit gradient, ADDED to
+ * the outputs (so it composes with moe_route_bwd, which writes them):
+ *   dw_router[h,e] += sum_t x[t,h] * dlogit[t,e]      (fp32 [H,E])
+ *   dx_router[t,h] += sum_e dlogit[t,e] * w_router[h,e] (fp32 [T,H])
+ * x [T,H] bf16 in token order; dlogit [T,E] fp32.  Every sum runs in a fixed
+ * order.  ws: at least moe_route_bwd_dense_workspace_bytes(T,H,E) bytes.
+ */
+moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t* x,
+                                 const float* w_router, const float* dlogit, float* dw_router,
+                                 float* dx_router, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,19 +73,20 @@ FAKE = 0x1000  # never dereferenced: every call below is rejected on the host
 
 def test_route_rejects(lib):
     f = lib.moe_route
-    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
+    # x, w_router, bias, topk_idx, topk_w, topk_s, scores, ws
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]
     big = 1 << 30
-    ok = [_p(FAKE)] * 6 + [_p(FAKE)]
+    ok = [_p(FAKE)] * 7 + [_p(FAKE)]
     assert f(8, 64, 8, 9, *ok, big, _p(None)) == 1          # K > E
     assert f(8, 64, 8, 0, *ok, big, _p(None)) == 1          # K = 0
     assert f(-1, 64, 8, 2, *ok, big, _p(None)) == 1         # T < 0
     assert f(8, 96, 8, 2, *ok, big, _p(None)) == 2          # H % 64
     assert f(8, 64, 200, 2, *ok, big, _p(None)) == 2        # E > 128
     assert f(8, 64, 32, 17, *ok, big, _p(None)) == 2        # K > 16
-    assert f(8, 64, 8, 2, _p(None), *[_p(FAKE)] * 6, big, _p(None)) == 1  # null x
+    assert f(8, 64, 8, 2, _p(None), *[_p(FAKE)] * 7, big, _p(None)) == 1  # null x
     assert f(8, 64, 8, 2, *ok, 16, _p(None)) == 3           # workspace too small
-    assert f(8, 64, 8, 2, *[_p(FAKE)] * 6, _p(None), big, _p(None)) == 3  # no workspace
-    assert f(0, 64, 8, 2, *[_p(None)] * 7, 0, _p(None)) == 0   # T = 0 no-op
+    assert f(8, 64, 8, 2, *[_p(FAKE)] * 7, _p(None), big, _p(None)) == 3  # no workspace
+    assert f(0, 64, 8, 2, *[_p(None)] * 8, 0, _p(None)) == 0   # T = 0 no-op
     lib.moe_last_error.restype = ctypes.c_char_p
     f(8, 64, 8, 9, *ok, big, _p(None))
     assert b"K > E" in lib.moe_last_error()
@@ -152,3 +153,43 @@ def test_backward_steps_reject(lib):
         assert f(4, 200, 64, 32, *seg, *ops, _p(None)) == 1, name            # rows % 128
         assert f(2, 256, 64, 32, _p(None), _p(None), _p(None), *ops, _p(None)) == 1, name
         assert f(4, 256, 64, 32, *seg, _p(None), *ops[1:], _p(None)) == 1, name  # null operand
+
+
+def test_balance_rejects(lib):
+    f = lib.moe_bias_update
+    f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+    assert f(0, _p(FAKE), _p(FAKE), 0.1, _p(None)) == 1      # E = 0
+    assert f(129, _p(FAKE), _p(FAKE), 0.1, _p(None)) == 2    # E > 128
+    assert f(8, _p(None), _p(FAKE), 0.1, _p(None)) == 1      # null counts
+
+    f = lib.moe_seq_balance_fwd
+    f.argtypes = ([ctypes.c_int32] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_float] +
+                  [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p])
+    big = 1 << 30
+    ok = [_p(FAKE)] * 2
+    assert f(8, 8, 2, 3, *ok, 0.1, *[_p(FAKE)] * 3, big, _p(None)) == 1   # T % seq_len
+    assert f(8, 8, 9, 4, *ok, 0.1, *[_p(FAKE)] * 3, big, _p(None)) == 1   # K > E
+    assert f(8, 200, 2, 4, *ok, 0.1, *[_p(FAKE)] * 3, big, _p(None)) == 2  # E > 128
+    assert f(8, 8, 2, 0, *ok, 0.1, *[_p(FAKE)] * 3, big, _p(None)) == 1   # seq_len = 0
+    assert f(8, 8, 2, 4, *ok, 0.1, _p(None), _p(FAKE), _p(FAKE), big, _p(None)) == 1  # null loss
+    assert f(8, 8, 2, 4, *ok, 0.1, *[_p(FAKE)] * 3, 4, _p(None)) == 3     # workspace too small
+
+    f = lib.moe_seq_balance_bwd
+    f.argtypes = ([ctypes.c_int32] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_float] +
+                  [ctypes.c_void_p] * 3)
+    assert f(8, 8, 2, 3, _p(FAKE), _p(FAKE), 0.1, _p(None), _p(FAKE), _p(None)) == 1  # T % seq_len
+    assert f(8, 8, 2, 4, _p(FAKE), _p(FAKE), 0.1, _p(None), _p(None), _p(None)) == 1  # null dlogit
+
+    f = lib.moe_route_bwd_dense
+    f.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(8, 96, 8, *[_p(FAKE)] * 6, big, _p(None)) == 2      # H % 64
+    assert f(8, 64, 200, *[_p(FAKE)] * 6, big, _p(None)) == 2    # E > 128
+    assert f(8, 64, 8, *[_p(FAKE)] * 5, _p(None), big, _p(None)) == 3   # no workspace
+    assert f(8, 64, 8, *[_p(FAKE)] * 6, 4, _p(None)) == 3        # workspace too small
+    assert f(0, 64, 8, *[_p(None)] * 6, 0, _p(None)) == 0        # T = 0 no-op
+
+    lib.moe_seq_balance_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_route_bwd_dense_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.moe_seq_balance_workspace_bytes(8192, 128, 4096) > 0
+    assert lib.moe_seq_balance_workspace_bytes(8192, 128, 3000) == 0
+    assert lib.moe_route_bwd_dense_workspace_bytes(8192, 5120, 128) > 0
