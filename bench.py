@@ -21,7 +21,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
+
+# load balancing: sequences of 8192 tokens (the pre-training context length),
+# balance-loss coefficient and bias step (values of the DeepSeek recipe's order)
+SEQ_LEN, ALPHA, GAMMA = 8192, 1e-4, 1e-3
+BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
 
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
@@ -101,7 +107,13 @@ class Layer:
             dact_sh=e(T, 2 * SF), dx_sh=e(T, H), dw1_sh=e(1, 2 * SF, H), dw2_sh=e(1, H, SF),
             dw_router=e(H, E, dt=f32), dx_router=e(T, H, dt=f32),
             rb_ws=e(M.moe_route_bwd_workspace_bytes(T, H, E, K), dt=torch.uint8),
-            dx=e(T, H))
+            dx=e(T, H),
+            # load balancing (sequence-wise loss over sequences of SEQ_LEN tokens, bias step)
+            scores=e(T, E, dt=f32), seq_f=e(max(T // SEQ_LEN, 1), E, dt=f32), loss=e(1, dt=f32),
+            seq_ws=e(max(M.moe_seq_balance_workspace_bytes(T, E, SEQ_LEN), 1), dt=torch.uint8),
+            dloss=torch.ones(1, dtype=f32, device=dev), dlogit_bal=e(T, E, dt=f32),
+            dense_ws=e(max(M.moe_route_bwd_dense_workspace_bytes(T, H, E), 1), dt=torch.uint8),
+            bias_train=g["bias"].clone())
         self.ev = None
 
     # the twelve grouped-GEMM launches of one step, in launch order
@@ -112,18 +124,22 @@ class Layer:
 
     def _gemm(self, name, ev, fn):
         """Launch one grouped GEMM, bracketed by events when ev is a dict."""
-        if ev is not None:
+        if ev is not None and name in ev:
             ev[name][0].record()
         fn()
-        if ev is not None:
+        if ev is not None and name in ev:
             ev[name][1].record()
 
-    def forward(self, ev=None):
+    def forward(self, ev=None, balance=False):
         M, g, b, K = self.M, self.g, self.b, self.K
         p = b["perm"]
         seg = (p["offsets"], p["counts"], p["tile_expert"])
         M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
-                    ws=b["route_ws"])
+                    ws=b["route_ws"], scores=b["scores"] if balance else None)
+        if balance:
+            self._gemm("seq_loss_fwd", ev, lambda: M.moe_seq_balance_fwd(
+                b["scores"], b["topk_idx"], SEQ_LEN, ALPHA, loss=b["loss"], seq_f=b["seq_f"],
+                ws=b["seq_ws"]))
         M.moe_permute(b["topk_idx"], g["x"], self.E, out=p, ws=b["perm_ws"])
         self._gemm("gate_up_fwd", ev, lambda: M.moe_grouped_gate_up_fwd(
             p["x_rows"], g["w1"], *seg, act=b["act"], h=b["h"]))
@@ -135,7 +151,7 @@ class Layer:
             b["h_sh"], self.w2f, y_rows=b["y_sh"]))
         M.moe_combine(b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"])
 
-    def backward(self, ev=None):
+    def backward(self, ev=None, balance=False):
         M, g, b = self.M, self.g, self.b
         p = b["perm"]
         seg = (p["offsets"], p["counts"], p["tile_expert"])
@@ -162,7 +178,18 @@ class Layer:
         M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
                         p["offsets"], p["counts"], dw_router=b["dw_router"],
                         dx_router=b["dx_router"], ws=b["rb_ws"])
+        if balance:
+            self._gemm("seq_loss_bwd", ev, lambda: M.moe_seq_balance_bwd(
+                b["scores"], b["seq_f"], self.K, SEQ_LEN, ALPHA, b["dloss"], dlogit=b["dlogit_bal"]))
+            self._gemm("route_bwd_dense", ev, lambda: M.moe_route_bwd_dense(
+                g["x"], g["w_router"], b["dlogit_bal"], b["dw_router"], b["dx_router"],
+                ws=b["dense_ws"]))
         M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+        if balance:
+            # the bias step on this batch's loads (a copy of the bias, so that
+            # every timed step routes the same way)
+            self._gemm("bias_update", ev, lambda: M.moe_bias_update(
+                p["counts"], b["bias_train"], GAMMA))
 
 
 def gemm_launch_flops(w, name):
@@ -296,6 +323,38 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
 
+    # the step with load balancing (balance loss forward/backward, its dense
+    # router gradients, the bias step), and each of those launches
+    bal = None
+    if backward:
+        def bal_step(ev=None):
+            layer.forward(ev, balance=True)
+            layer.backward(ev, balance=True)
+        for _ in range(2):
+            bal_step()
+        bevs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for n in BALANCE_OPS} for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for i in range(args.steps):
+            bal_step(bevs[i])
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bal_ms = b0.elapsed_time(b1) / args.steps
+        op_us = {n: 1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in bevs]))
+                 for n in BALANCE_OPS}
+        dense_flops = 2 * 2.0 * w.T * w.H * w.E
+        dense_tf = dense_flops / (op_us["route_bwd_dense"] * 1e-6) / 1e12
+        bal = {"seq_len": SEQ_LEN, "alpha": ALPHA, "gamma": GAMMA,
+               "ms_per_step": round(bal_ms, 4),
+               "extra_ms": round(bal_ms - ms, 4),
+               **{f"{n}_us": round(op_us[n], 2) for n in BALANCE_OPS},
+               "route_bwd_dense_roofline": {"bound": "alu", "achieved": round(dense_tf, 2),
+                                            "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                                            "frac": round(dense_tf / PEAK_FP32_TFLOPS, 4)}}
+
     flops = useful_flops(w, backward)
     tflops = flops / (ms * 1e-3) / 1e12
     fwd_tflops = useful_flops(w, False) / (fwd_ms * 1e-3) / 1e12
@@ -340,6 +399,8 @@ def main():
                      **traffic_of(dom, w)},
         "gemm_launches": launches,
     }
+    if bal is not None:
+        out["load_balancing"] = bal
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens)
     print(json.dumps(out), flush=True)

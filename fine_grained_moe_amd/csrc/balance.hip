@@ -52,11 +52,12 @@ __global__ void __launch_bounds__(EMAX) bias_update_kernel(int E, const int32_t*
 }
 
 // ---- sequence-wise balance loss, forward ---------------------------------
-// Pass 1: workgroup (sequence b, chunk c) takes CH tokens of sequence b, one
-// wave per token in turn; lane l owns experts l and l + 64.  It adds up, per
-// expert, the normalised scores s[t,e] / sum_j s[t,j] and the picks of its
-// tokens, then writes the chunk's partial sums (waves added in wave order).
-constexpr int CH = 64, NT = 256, NW = NT / 64;
+// Pass 1: workgroup (sequence b, chunk c) takes CH tokens of sequence b;
+// wave w takes TPW of them (all their loads issued first), lane l owns
+// experts l and l + 64.  It adds up, per expert, the normalised scores
+// s[t,e] / sum_j s[t,j] and the picks of its tokens in token order, then
+// writes the chunk's partial sums (waves added in wave order).
+constexpr int CH = 32, NT = 256, NW = NT / 64, TPW = CH / NW;
 
 __global__ void __launch_bounds__(NT) seq_partial_kernel(int T, int E, int K, int L, int nch,
                                                          const float* __restrict__ scores,
@@ -70,22 +71,30 @@ __global__ void __launch_bounds__(NT) seq_partial_kernel(int T, int E, int K, in
   const int t_lo = b * L + c * CH, t_hi = min(b * L + min(L, (c + 1) * CH), T);
   float acc[2] = {0.f, 0.f};
   int cnt[2] = {0, 0};
-  for (int t = t_lo + wave; t < t_hi; t += NW) {
-    float s[2];
+  float s[TPW][2];
+  int pick[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = t_lo + wave * TPW + j;
+    const bool ok = t < t_hi;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int e = lane + 64 * q;
-      s[q] = e < E ? scores[(int64_t)t * E + e] : 0.f;
+      s[j][q] = (ok && e < E) ? scores[(int64_t)t * E + e] : 0.f;
     }
-    const float inv = 1.0f / wave_sum(s[0] + s[1]);
-    const int pick = lane < K ? topk_idx[(int64_t)t * K + lane] : -1;
+    pick[j] = (ok && lane < K) ? topk_idx[(int64_t)t * K + lane] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    if (t_lo + wave * TPW + j >= t_hi) break;
+    const float inv = 1.0f / wave_sum(s[j][0] + s[j][1]);
     for (int k = 0; k < K; ++k) {
-      const int ek = __shfl(pick, k, 64);
+      const int ek = __shfl(pick[j], k, 64);
       cnt[0] += ek == lane;
       cnt[1] += ek == lane + 64;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) acc[q] += s[q] * inv;
+    for (int q = 0; q < 2; ++q) acc[q] += s[j][q] * inv;
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -122,6 +131,7 @@ __global__ void __launch_bounds__(EMAX) seq_final_kernel(int E, int K, int L, in
   if (e < E) {
     float p = 0.f;
     int n = 0;
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) {
       p += psum[((int64_t)b * nch + c) * E + e];
       n += picks[((int64_t)b * nch + c) * E + e];
