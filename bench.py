@@ -5,7 +5,7 @@ grouped SwiGLU GEMMs, combine, and their backward) over T=8192 tokens at
 dots.llm1 shapes (H=5120, 128 routed experts of width 1408, top-6, 2 shared
 experts), synthetic seeded inputs resident in HBM.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-balance]
 """
 from __future__ import annotations
 
@@ -36,14 +36,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "cce355c5c8f0c9a71a5e3b8311bb15ae04481654798837fef0b792423e701d80"
+TRAFFIC_SOURCE_SHA256 = "509c823829f4cf622f8e8fec50107a2be80ed95303685334282c76c2359f62f3"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3092372.0, 405504.0), "down_fwd": (1157367.5, 491520.0),
+    "gate_up_fwd": (3094212.0, 405504.0), "down_fwd": (1152267.7, 491520.0),
     "shared_gate_up_fwd": (348239.8, 135168.0), "shared_down_fwd": (180287.4, 81920.0),
-    "down_dgrad": (1578507.5, 270336.0), "gate_up_dgrad": (2492468.0, 491520.0),
-    "down_wgrad": (591835.3, 1802240.0), "gate_up_wgrad": (1089884.3, 3604480.0),
-    "shared_down_dgrad": (352406.0, 90112.0), "shared_gate_up_dgrad": (360515.9, 81920.0),
-    "shared_down_wgrad": (217146.4, 28160.0), "shared_gate_up_wgrad": (434235.6, 56320.0),
+    "down_dgrad": (1638448.1, 270336.0), "gate_up_dgrad": (2547234.7, 491520.0),
+    "down_wgrad": (590208.3, 1802240.0), "gate_up_wgrad": (1110427.7, 3604480.0),
+    "shared_down_dgrad": (352372.4, 90112.0), "shared_gate_up_dgrad": (360515.4, 81920.0),
+    "shared_down_wgrad": (217146.3, 28160.0), "shared_gate_up_wgrad": (434235.7, 56320.0),
 }
 
 
@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the same batch the CPU oracle runs on")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="skip the timing of the step with load balancing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device to device (known HBM bytes, for scaling "
                          "hardware byte counters)")
@@ -326,7 +328,7 @@ def main():
     # the step with load balancing (balance loss forward/backward, its dense
     # router gradients, the bias step), and each of those launches
     bal = None
-    if backward:
+    if backward and not args.no_balance:
         def bal_step(ev=None):
             layer.forward(ev, balance=True)
             layer.backward(ev, balance=True)
