@@ -376,6 +376,8 @@ moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t
   if (T == 0) return MOE_OK;
   REQUIRE(x && w_router && dlogit && dw_router && dx_router, MOE_ERR_INVALID_ARGUMENT,
           "null pointer");
+  REQUIRE(((uintptr_t)dx_router & 15) == 0 && ((uintptr_t)ws & 255) == 0,
+          MOE_ERR_INVALID_ARGUMENT, "dx_router must be 16-byte and ws 256-byte aligned");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_dense_workspace_bytes(T, H, E),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   return hip_status(moe::launch_route_bwd_dense(T, H, E, x, w_router, dlogit, dw_router,

@@ -195,170 +195,111 @@ __global__ void __launch_bounds__(NT) seq_bwd_kernel(int T, int E, int L, int B,
 }
 
 // ---- router gradients of a dense logit gradient --------------------------
-// fp32 products on the vector ALU, 128 x 128 output tiles of 256 threads,
-// each thread an 8 x 8 block; k advances 16 at a time through a
-// double-buffered LDS stage whose rows are k.  Both operands are staged
-// k-major, so a thread reads its 8 rows and 8 columns as two 16-byte words
-// each.
-constexpr int GT = 128, GK = 16, GNT = 256;
+// Both products run on the bf16 matrix cores through the grouped-GEMM kernel.
+// Every fp32 operand v is split exactly into three bf16 parts,
+//   hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid),
+// whose sum is v to about 2^-27 |v|.  x is bf16 already.
+//   dW_r = x^T dlogit          = x^T (d_hi + d_mid + d_lo): three exact products
+//   dx_r = dlogit W_r^T        = the six part products down to 2^-16 of the
+//                                leading one (hi.hi, hi.mid, mid.hi, hi.lo,
+//                                lo.hi, mid.mid); the three left out are below
+//                                fp32 rounding
+// Each part block is padded to EP = E rounded up to 8 columns (zeros).  dx_r
+// takes one GEMM with the six blocks laid side by side along K; dW_r takes one
+// K-grouped GEMM over G token slices with the three parts side by side along
+// N, whose fp32 partial results are then added in a fixed order.
+__device__ __forceinline__ void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
 
-// rows padded by 16 bytes so that the transposing stores of one k column
-// fall into different banks
-constexpr int GP = GT + 4;
-struct alignas(16) Stage {
-  float a[GK][GP];
-  float b[GK][GP];
-};
+// part order of the six K blocks: dlogit side and W_r side
+__constant__ int kPartA[6] = {0, 0, 1, 0, 2, 1};
+__constant__ int kPartB[6] = {0, 1, 0, 2, 0, 1};
 
-__device__ __forceinline__ void fma_block(const Stage& st, int ty, int tx, float (&acc)[8][8]) {
+// src [R, E] fp32 -> six [R, EP] blocks along each row of dst6 ([R, 6 EP],
+// parts in `order`), and, when dst3 is given, the three parts in order along
+// each row of dst3 ([R, 3 EP]).  Columns E..EP-1 are zero.
+__global__ void __launch_bounds__(256) split_rows_kernel(int R, int E, int EP, int side,
+                                                         const float* __restrict__ src,
+                                                         uint16_t* __restrict__ dst6,
+                                                         uint16_t* __restrict__ dst3) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)R * EP) return;
+  const int64_t r = i / EP;
+  const int e = (int)(i % EP);
+  const float v = e < E ? src[r * E + e] : 0.f;
+  uint16_t part[3];
+  split3(v, part[0], part[1], part[2]);
+  const int* order = side == 0 ? kPartA : kPartB;
 #pragma unroll
-  for (int k = 0; k < GK; ++k) {
-    const f32x4 a0 = *(const f32x4*)&st.a[k][ty * 4];
-    const f32x4 a1 = *(const f32x4*)&st.a[k][64 + ty * 4];
-    const f32x4 b0 = *(const f32x4*)&st.b[k][tx * 4];
-    const f32x4 b1 = *(const f32x4*)&st.b[k][64 + tx * 4];
-    const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  for (int q = 0; q < 6; ++q) dst6[r * 6 * EP + q * EP + e] = part[order[q]];
+  if (dst3) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    for (int q = 0; q < 3; ++q) dst3[r * 3 * EP + q * EP + e] = part[q];
   }
 }
 
-// row i of a thread's block is tile row (i < 4 ? ty*4 + i : 64 + ty*4 + i-4)
-__device__ __forceinline__ int blk_row(int t, int i) { return i < 4 ? t * 4 + i : 64 + t * 4 + i - 4; }
-
-// dx[t,h] += sum_e dlogit[t,e] * w[h,e]: tile (128 tokens, 128 h), k = e.
-// Stage loads: dlogit rows t (k contiguous) and w rows h (k contiguous), both
-// transposed into the k-major stage; elements past T, H or E read as zero.
-__global__ void __launch_bounds__(GNT) dense_dx_kernel(int T, int H, int E,
-                                                       const float* __restrict__ dlogit,
-                                                       const float* __restrict__ w,
-                                                       float* __restrict__ dx) {
-  __shared__ Stage st[2];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int t0 = blockIdx.y * GT, h0 = blockIdx.x * GT;
-  // loader: thread covers (row lr + 16 i, k lk) for i < 8
-  const int lk = tid & 15, lr = tid >> 4;
-  float acc[8][8] = {};
-  auto load = [&](int buf, int k0) {
-    const int k = k0 + lk;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = lr + 16 * i;
-      const int t = t0 + r, h = h0 + r;
-      st[buf].a[lk][r] = (t < T && k < E) ? dlogit[(int64_t)t * E + k] : 0.f;
-      st[buf].b[lk][r] = (h < H && k < E) ? w[(int64_t)h * E + k] : 0.f;
-    }
-  };
-  const int nk = (E + GK - 1) / GK;
-  load(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load((kt + 1) & 1, (kt + 1) * GK);
-    fma_block(st[kt & 1], ty, tx, acc);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = t0 + blk_row(ty, i);
-    if (t >= T) continue;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int h = h0 + half * 64 + tx * 4;
-      if (h >= H) continue;  // H % 64 == 0: a 4-column group is all in or all out
-      f32x4* p = (f32x4*)(dx + (int64_t)t * H + h);
-      f32x4 v = *p;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += acc[i][half * 4 + j];
-      *p = v;
-    }
-  }
+// token slices of the weight-gradient product
+__global__ void seg_kernel(int G, int S, int T, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ counts) {
+  const int g = threadIdx.x;
+  if (g > G) return;
+  const int o = min(g * S, T);
+  offsets[g] = o;
+  if (g < G) counts[g] = min(S, T - o);
 }
 
-// Split-k partial of dW_r: part[s][h,e] = sum over tokens t of slice s of
-// x[t,h] * dlogit[t,e].  Tile (128 h, 128 e), k = t; x rows are h-contiguous
-// and dlogit rows e-contiguous, so both stage without a transpose.
-__global__ void __launch_bounds__(GNT) dense_dw_kernel(int T, int H, int E, int t_per_slice,
-                                                       const uint16_t* __restrict__ x,
-                                                       const float* __restrict__ dlogit,
-                                                       float* __restrict__ part) {
-  __shared__ Stage st[2];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int h0 = blockIdx.x * GT, slice = blockIdx.y;
-  const int tb = slice * t_per_slice, te = min(T, tb + t_per_slice);
-  // loader: thread covers k row kr and the 8 consecutive columns lc*8
-  const int kr = tid >> 4, lc = tid & 15;
-  float acc[8][8] = {};
-  auto load = [&](int buf, int k0) {
-    {
-      const int t = k0 + kr;
-      const int h = h0 + lc * 8;
-      float xv[8], dv[8];
-      if (t < te && h < H) {
-        const u32x4 raw = *(const u32x4*)(x + (int64_t)t * H + h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xv[2 * j] = lo_bf16(raw[j]);
-          xv[2 * j + 1] = hi_bf16(raw[j]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = lc * 8 + j;
-        dv[j] = (t < te && e < E) ? dlogit[(int64_t)t * E + e] : 0.f;
-      }
-      *(f32x4*)&st[buf].a[kr][lc * 8] = f32x4{xv[0], xv[1], xv[2], xv[3]};
-      *(f32x4*)&st[buf].a[kr][lc * 8 + 4] = f32x4{xv[4], xv[5], xv[6], xv[7]};
-      *(f32x4*)&st[buf].b[kr][lc * 8] = f32x4{dv[0], dv[1], dv[2], dv[3]};
-      *(f32x4*)&st[buf].b[kr][lc * 8 + 4] = f32x4{dv[4], dv[5], dv[6], dv[7]};
-    }
-  };
-  const int nk = (te - tb + GK - 1) / GK;
-  if (nk > 0) {
-    load(0, tb);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load((kt + 1) & 1, tb + (kt + 1) * GK);
-    fma_block(st[kt & 1], ty, tx, acc);
-    __syncthreads();
-  }
-  float* out = part + (int64_t)slice * H * GT;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int h = h0 + blk_row(ty, i);
-    if (h >= H) continue;
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-      *(f32x4*)(out + (int64_t)h * GT + half * 64 + tx * 4) =
-          f32x4{acc[i][half * 4], acc[i][half * 4 + 1], acc[i][half * 4 + 2], acc[i][half * 4 + 3]};
-  }
-}
-
-// dW_r[h,e] += sum_s part[s][h,e], slices in order.
-__global__ void __launch_bounds__(256) dense_dw_reduce_kernel(int H, int E, int slices,
-                                                              const float* __restrict__ part,
-                                                              float* __restrict__ dw) {
+// dW_r[h,e] += sum over slices g and parts p of part[g][h][p EP + e]
+__global__ void __launch_bounds__(256) dw_reduce_kernel(int H, int E, int EP, int G,
+                                                        const float* __restrict__ part,
+                                                        float* __restrict__ dw) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)H * E) return;
-  const int64_t h = i / E, e = i % E;
+  const int64_t h = i / E;
+  const int e = (int)(i % E);
   float s = dw[i];
-  for (int k = 0; k < slices; ++k) s += part[((int64_t)k * H + h) * GT + e];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) s += part[((int64_t)g * H + h) * 3 * EP + p * EP + e];
   dw[i] = s;
 }
 
-// token slices of the dW_r split: enough workgroups to cover the CUs twice
-__host__ inline int dw_slices(int T, int H) {
-  const int tiles = (H + GT - 1) / GT;
-  int s = (512 + tiles - 1) / tiles;
-  const int by_t = (T + 255) / 256;  // at least 256 tokens per slice
-  s = s < by_t ? s : by_t;
-  return s < 1 ? 1 : s;
+// token slices for dW_r: enough workgroups for the CUs (the grouped kernel
+// tiles 256 x 256), at least 256 tokens each
+__host__ inline int dw_slices(int T, int H, int EP) {
+  const int tiles = ((H + 255) / 256) * ((3 * EP + 255) / 256);
+  int g = (512 + tiles - 1) / tiles;
+  const int by_t = (T + 255) / 256;
+  g = g < by_t ? g : by_t;
+  g = g < 255 ? g : 255;  // seg_kernel: one thread per slice boundary
+  return g < 1 ? 1 : g;
+}
+
+struct DenseWs {
+  uint16_t *a6, *w6, *d3;
+  int32_t *offsets, *counts;
+  float* part;
+  size_t bytes;
+};
+
+__host__ inline size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+
+__host__ inline DenseWs dense_ws(int T, int H, int E, void* base) {
+  const int EP = (E + 7) / 8 * 8, G = dw_slices(T, H, EP);
+  const uintptr_t p = (uintptr_t)base;
+  DenseWs w;
+  size_t o = 0;
+  w.a6 = (uint16_t*)(p + o); o += al256((size_t)T * 6 * EP * 2);
+  w.w6 = (uint16_t*)(p + o); o += al256((size_t)H * 6 * EP * 2);
+  w.d3 = (uint16_t*)(p + o); o += al256((size_t)T * 3 * EP * 2);
+  w.offsets = (int32_t*)(p + o); o += al256((size_t)(G + 1) * 4);
+  w.counts = (int32_t*)(p + o); o += al256((size_t)G * 4);
+  w.part = (float*)(p + o); o += al256((size_t)G * H * 3 * EP * 4);
+  w.bytes = o;
+  return w;
 }
 
 }  // namespace bal
@@ -402,23 +343,32 @@ hipError_t launch_seq_balance_bwd(int T, int E, int L, const float* scores, cons
 }
 
 size_t route_bwd_dense_workspace_bytes(int T, int H, int E) {
-  (void)E;
-  return (size_t)bal::dw_slices(T, H) * H * bal::GT * 4;
+  return bal::dense_ws(T, H, E, nullptr).bytes;
 }
 
 hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const float* w_router,
                                   const float* dlogit, float* dw_router, float* dx_router,
                                   void* ws, hipStream_t s) {
-  const int slices = bal::dw_slices(T, H);
-  const int t_per = ((T + slices - 1) / slices + bal::GK - 1) / bal::GK * bal::GK;
-  float* part = (float*)ws;
-  hipLaunchKernelGGL(bal::dense_dx_kernel, dim3((H + bal::GT - 1) / bal::GT, (T + bal::GT - 1) / bal::GT),
-                     dim3(bal::GNT), 0, s, T, H, E, dlogit, w_router, dx_router);
-  hipLaunchKernelGGL(bal::dense_dw_kernel, dim3((H + bal::GT - 1) / bal::GT, slices), dim3(bal::GNT),
-                     0, s, T, H, E, t_per, x, dlogit, part);
+  const int EP = (E + 7) / 8 * 8, G = bal::dw_slices(T, H, EP);
+  const bal::DenseWs w = bal::dense_ws(T, H, E, ws);
+  const int S = (T + G - 1) / G;
+  hipLaunchKernelGGL(bal::split_rows_kernel, dim3((unsigned)(((int64_t)T * EP + 255) / 256)),
+                     dim3(256), 0, s, T, E, EP, 0, dlogit, w.a6, w.d3);
+  hipLaunchKernelGGL(bal::split_rows_kernel, dim3((unsigned)(((int64_t)H * EP + 255) / 256)),
+                     dim3(256), 0, s, H, E, EP, 1, w_router, w.w6, (uint16_t*)nullptr);
+  hipLaunchKernelGGL(bal::seg_kernel, dim3(1), dim3(256), 0, s, G, S, T, w.offsets, w.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dx_r += [d parts] . [W_r parts]^T, K = 6 EP
+  e = launch_gemm_f32_nt(T, H, 6 * EP, w.a6, 6 * EP, w.w6, 6 * EP, dx_router, H, true, s);
+  if (e != hipSuccess) return e;
+  // part[g] = x_g^T [d_hi | d_mid | d_lo]_g, then dW_r += the sum of the parts
+  e = launch_gemm_f32_tn_grouped(G, w.offsets, w.counts, T, H, 3 * EP, x, H, w.d3, 3 * EP, w.part,
+                                 3 * EP, (int64_t)H * 3 * EP, s);
+  if (e != hipSuccess) return e;
   const int64_t n = (int64_t)H * E;
-  hipLaunchKernelGGL(bal::dense_dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     H, E, slices, part, dw_router);
+  hipLaunchKernelGGL(bal::dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, H,
+                     E, EP, G, w.part, dw_router);
   return hipGetLastError();
 }
 

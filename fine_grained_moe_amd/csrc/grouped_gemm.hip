@@ -115,7 +115,7 @@ constexpr int GROUP_M = 4;  // m-tiles per rasterization group (row-grouped, non
 constexpr int KGROUP_GM = 4;
 
 enum Src { KC = 0, MC = 1 };
-enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2 };
+enum Epi { EPI_SWIGLU_FWD = 0, EPI_STORE = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
 enum Mode { MGROUP = 0, KGROUP = 1 };
 
 struct Args {
@@ -134,6 +134,8 @@ struct Args {
   int64_t strideC;       // KGROUP: elements between consecutive groups' C
   int F;                 // SWIGLU: expert width (gate/up split)
   int n_mtiles, n_ntiles, G;
+  float* Cf;             // F32: fp32 output (row-major, ldc)
+  int acc_out;           // F32: add to Cf instead of writing it
 };
 
 // MN-contig tile of BK k-rows x C columns.  A 1 KB region holds KPR k-rows.
@@ -633,6 +635,31 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
           }
       store_plane(gplane, a.C, 2 * (int64_t)a.F, m0, seg_hi, n0 + part * PC, a.F);  // dgate
     }
+  } else if constexpr (EPI == EPI_F32) {
+    // fp32 results straight from the accumulators (four consecutive columns
+    // per lane and group, 16-byte accesses), written or added to the output
+    float* Cf = a.Cf + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
+    const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
+    const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t row = row0 + a_base[i] + mrow;
+          const int col = n0 + b_base[j] + 8 * g + csub;
+          if (row < rows_lim && col < a.N) {
+            f32x4* p = (f32x4*)(Cf + row * a.ldc + col);
+            f32x4 v = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                       acc[i][j][4 * g + 3]};
+            if (a.acc_out) {
+              const f32x4 o = *p;
+              v = f32x4{o[0] + v[0], o[1] + v[1], o[2] + v[2], o[3] + v[3]};
+            }
+            *p = v;
+          }
+        }
   } else {  // EPI_STORE
     uint16_t* Cg = a.C + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
     const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
@@ -771,6 +798,35 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.n_mtiles = (2 * F + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (H + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
   return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+}
+
+// C[M,N] (+)= A[M,K] . B[N,K]^T: bf16 operands with K-contiguous rows, fp32
+// output, one dense group.  K, lda, ldb multiples of 8; N, ldc multiples of 4.
+hipError_t launch_gemm_f32_nt(int64_t M, int N, int K, const uint16_t* A, int lda,
+                              const uint16_t* B, int ldb, float* C, int ldc, bool accumulate,
+                              hipStream_t s) {
+  Args a = {};
+  a.A = A; a.B = B; a.Cf = C; a.acc_out = accumulate ? 1 : 0;
+  a.m_rows = M; a.N = N; a.K = K; a.F = 0;
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc; a.strideB = 0; a.G = 1;
+  return launch_rows<KC, KC, EPI_F32>(a, CfgRows::BN, CfgWide::BN, N, s);
+}
+
+// C_g[M,N] = sum over the rows r of segment g of A[r,m] . B[r,n] (A [rows,M],
+// B [rows,N], bf16 row-major), fp32 C_g at C + g * strideC.  M, N, lda, ldb
+// multiples of 8.
+hipError_t launch_gemm_f32_tn_grouped(int G, const int32_t* offsets, const int32_t* counts,
+                                      int64_t rows, int M, int N, const uint16_t* A, int lda,
+                                      const uint16_t* B, int ldb, float* C, int ldc,
+                                      int64_t strideC, hipStream_t s) {
+  Args a = {};
+  a.A = A; a.B = B; a.Cf = C; a.acc_out = 0;
+  a.offsets = offsets; a.counts = counts;
+  a.m_rows = rows; a.M = M; a.N = N; a.F = 0;
+  a.lda = lda; a.ldb = ldb; a.ldc = ldc; a.strideB = 0; a.strideC = strideC;
+  a.n_mtiles = (M + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (N + CfgWgrad::BN - 1) / CfgWgrad::BN;
+  a.G = G;
+  return launch<CfgWgrad, MC, MC, EPI_F32, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
 }
 
 }  // namespace moe

@@ -42,6 +42,14 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
                                 const int32_t* counts, const uint16_t* dact,
                                 const uint16_t* x_rows, uint16_t* dw1, hipStream_t s);
 
+hipError_t launch_gemm_f32_nt(int64_t M, int N, int K, const uint16_t* A, int lda,
+                              const uint16_t* B, int ldb, float* C, int ldc, bool accumulate,
+                              hipStream_t s);
+hipError_t launch_gemm_f32_tn_grouped(int G, const int32_t* offsets, const int32_t* counts,
+                                      int64_t rows, int M, int N, const uint16_t* A, int lda,
+                                      const uint16_t* B, int ldb, float* C, int ldc,
+                                      int64_t strideC, hipStream_t s);
+
 hipError_t launch_combine(int T, int H, int K, const uint16_t* y_rows, const int32_t* row_of,
                           const float* topk_w, const uint16_t* y_shared, uint16_t* y,
                           hipStream_t s);

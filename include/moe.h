@@ -346,8 +346,11 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
  * the outputs (so it composes with moe_route_bwd, which writes them):
  *   dw_router[h,e] += sum_t x[t,h] * dlogit[t,e]      (fp32 [H,E])
  *   dx_router[t,h] += sum_e dlogit[t,e] * w_router[h,e] (fp32 [T,H])
- * x [T,H] bf16 in token order; dlogit [T,E] fp32.  Every sum runs in a fixed
- * order.  ws: at least moe_route_bwd_dense_workspace_bytes(T,H,E) bytes.
+ * x [T,H] bf16 in token order; dlogit [T,E] fp32; dx_router 16-byte aligned.
+ * The products run on the bf16 matrix cores with every fp32 operand split
+ * exactly into three bf16 parts (fp32-level accuracy).  Every sum runs in a
+ * fixed order.  ws: at least moe_route_bwd_dense_workspace_bytes(T,H,E) bytes,
+ * 256-byte aligned.
  */
 moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t* x,
                                  const float* w_router, const float* dlogit, float* dw_router,
