@@ -295,8 +295,9 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   McLoad<BM, BK, NW> la_mc;
   KcLoad<BN, BK, NW> lb_kc;
   McLoad<BN, BK, NW> lb_mc;
+  // rows of the tile inside the segment (MGROUP)
+  const int rows_valid = (MODE == MGROUP) ? (int)min<int64_t>(BM, seg_hi - m0) : BM;
   if constexpr (MODE == MGROUP) {
-    const int rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
     rA = make_rsrc(a.A + m0 * a.lda, (uint32_t)rows_valid * a.lda * 2);
     la_kc.init([&](int r) -> uint32_t { return r < rows_valid ? (uint32_t)r * a.lda * 2 : kOOB; },
                wave, lane);
@@ -387,10 +388,12 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   // One k-step (16 deep) of the wave tile: WM x WN MFMAs on fragments that
   // were read from LDS one k-step earlier (double-buffered registers), so the
   // LDS latency of step s+1 hides behind the MFMAs of step s.
-  auto frags = [&](int kt, int kk, bf16x8* af, bf16x8* bfr) {
+  // (NL of the wave's WM row blocks take part, see below)
+  auto frags = [&](auto nl_c, int kt, int kk, bf16x8* af, bf16x8* bfr) {
+    constexpr int NL = decltype(nl_c)::value;
     const uint8_t* As = smem + (kt % STAGES) * Cfg::STAGE_BYTES;
     const uint8_t* Bs = As + Cfg::A_BYTES;
-    load_frags<ASRC, WM, BM, BK>(As, a_base, kk, lane, af);
+    load_frags<ASRC, NL, BM, BK>(As, a_base, kk, lane, af);
     load_frags<BSRC, WN, BN, BK>(Bs, b_base, kk, lane, bfr);
   };
 
@@ -405,8 +408,6 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
     for (int i = 0; i < LOADS; ++i) issue_one(s, i);
   wait_vmcnt<LOADS * (STAGES - 2)>();
   lds_barrier();
-  bf16x8 af[2][WM], bfr[2][WN];
-  frags(0, 0, af[0], bfr[0]);
 
   // each k-step issues PER_KK of the LOADS loads of stage kt+STAGES-1, so
   // when the last k-step of stage kt waits for stage kt+1, the loads issued
@@ -422,37 +423,65 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
                           ((Cfg::KK - 1) * PER_KK < LOADS ? (Cfg::KK - 1) * PER_KK : LOADS);
   static_assert(STAGES >= 2 && ISSUE_KK >= 1, "pipeline depth");
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt+STAGES-1 goes into the buffer stage kt-1 used; every wave
-    // finished reading that one before the barrier that preceded stage kt
-    const int nxt = kt + STAGES - 1;
+  // The main loop for a wave whose first NL row blocks (of 32 rows) hold rows
+  // of the segment: the other blocks are padding, whose MFMAs and fragment
+  // reads it skips (their results would be dropped).  Every wave issues the
+  // same loads, waits and barriers whatever its NL.
+  auto main_loop = [&](auto nl_c) {
+    constexpr int NL = decltype(nl_c)::value;
+    bf16x8 af[2][WM], bfr[2][WN];
+    if constexpr (NL > 0) frags(nl_c, 0, 0, af[0], bfr[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt+STAGES-1 goes into the buffer stage kt-1 used; every wave
+      // finished reading that one before the barrier that preceded stage kt
+      const int nxt = kt + STAGES - 1;
 #pragma unroll
-    for (int kk = 0; kk < Cfg::KK; ++kk) {
-      const int cur = kk & 1, nb = cur ^ 1;
-      if (kk + 1 < Cfg::KK) {
-        frags(kt, kk + 1, af[nb], bfr[nb]);
-      } else {
-        // stage kt+1 has landed once only the loads issued after it remain
-        wait_vmcnt<LATER>();
-        lds_barrier();
-        frags(kt + 1, 0, af[nb], bfr[nb]);
-      }
-      // keep the reads ahead of the MFMAs that hide their latency
-      __builtin_amdgcn_sched_barrier(0);
-      // this k-step's share of the next stage's DMA loads, between MFMAs
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-          const int t = i * WN + j;
-          const int li = kk * PER_KK + t;
-          if (t < PER_KK && li < LOADS) {
-            issue_one(nxt, li);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int kk = 0; kk < Cfg::KK; ++kk) {
+        const int cur = kk & 1, nb = cur ^ 1;
+        if (kk + 1 < Cfg::KK) {
+          if constexpr (NL > 0) frags(nl_c, kt, kk + 1, af[nb], bfr[nb]);
+        } else {
+          // stage kt+1 has landed once only the loads issued after it remain
+          wait_vmcnt<LATER>();
+          lds_barrier();
+          if constexpr (NL > 0) frags(nl_c, kt + 1, 0, af[nb], bfr[nb]);
         }
+        // keep the reads ahead of the MFMAs that hide their latency
+        __builtin_amdgcn_sched_barrier(0);
+        // this k-step's share of the next stage's DMA loads, between MFMAs
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            if (i < NL)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i],
+                                                                  acc[i][j], 0, 0, 0);
+            const int t = i * WN + j;
+            const int li = kk * PER_KK + t;
+            if (t < PER_KK && li < LOADS) {
+              issue_one(nxt, li);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+      }
     }
+  };
+  // live row blocks of this wave: routed 128-row tiles skip padding blocks
+  // one by one; other tiles run whole waves or none
+  const int nl_rows = (rows_valid - wm * WTM + 31) / 32;
+  const int nl = nl_rows <= 0 ? 0 : (nl_rows >= WM ? WM : nl_rows);
+  if constexpr (MODE == MGROUP && BM == kAlign && WM == 2) {
+    if (nl == 2)
+      main_loop(std::integral_constant<int, 2>{});
+    else if (nl == 1)
+      main_loop(std::integral_constant<int, 1>{});
+    else
+      main_loop(std::integral_constant<int, 0>{});
+  } else {
+    if (nl > 0)
+      main_loop(std::integral_constant<int, WM>{});
+    else
+      main_loop(std::integral_constant<int, 0>{});
   }
   wait_vmcnt<0>();
 
