@@ -467,9 +467,12 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
     }
   };
   // live row blocks of this wave: routed 128-row tiles skip padding blocks
-  // one by one; other tiles run whole waves or none
+  // one by one; other tiles run whole waves or none.  A wave whose columns
+  // all lie past N (the last column tile of an N that is not a multiple of
+  // the tile) has nothing to compute either.
   const int nl_rows = (rows_valid - wm * WTM + 31) / 32;
-  const int nl = nl_rows <= 0 ? 0 : (nl_rows >= WM ? WM : nl_rows);
+  const bool cols_live = (EPI == EPI_SWIGLU_FWD) || (a.N - n0 - wn * WTN > 0);
+  const int nl = (nl_rows <= 0 || !cols_live) ? 0 : (nl_rows >= WM ? WM : nl_rows);
   if constexpr (MODE == MGROUP && BM == kAlign && WM == 2) {
     if (nl == 2)
       main_loop(std::integral_constant<int, 2>{});
