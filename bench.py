@@ -35,14 +35,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "509c823829f4cf622f8e8fec50107a2be80ed95303685334282c76c2359f62f3"
+TRAFFIC_SOURCE_SHA256 = "91e714d91f315951e8409c651c0e33a13fa79ba80249cc42d72984f153664ff7"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3094212.0, 405504.0), "down_fwd": (1152267.7, 491520.0),
-    "shared_gate_up_fwd": (348239.8, 135168.0), "shared_down_fwd": (180287.4, 81920.0),
-    "down_dgrad": (1638448.1, 270336.0), "gate_up_dgrad": (2547234.7, 491520.0),
-    "down_wgrad": (590208.3, 1802240.0), "gate_up_wgrad": (1110427.7, 3604480.0),
-    "shared_down_dgrad": (352372.4, 90112.0), "shared_gate_up_dgrad": (360515.4, 81920.0),
-    "shared_down_wgrad": (217146.3, 28160.0), "shared_gate_up_wgrad": (434235.7, 56320.0),
+    "gate_up_fwd": (3089712.0, 405504.0), "down_fwd": (1143370.8, 491520.0),
+    "shared_gate_up_fwd": (348240.3, 135168.0), "shared_down_fwd": (180294.3, 81920.0),
+    "down_dgrad": (1881249.8, 270336.0), "gate_up_dgrad": (2585312.8, 491520.0),
+    "down_wgrad": (594303.3, 1802240.0), "gate_up_wgrad": (1095768.1, 3604480.0),
+    "shared_down_dgrad": (352382.0, 90112.0), "shared_gate_up_dgrad": (360522.4, 81920.0),
+    "shared_down_wgrad": (217162.8, 28160.0), "shared_gate_up_wgrad": (434252.2, 56320.0),
 }
 
 
