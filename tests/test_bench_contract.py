@@ -1,0 +1,30 @@
+"""The benchmark's command-line contract that needs no GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_gemm_flop_and_byte_accounting():
+    """Useful flops of the twelve GEMM launches add up to the layer's GEMM
+    flops (3 * (K+S) * 6HF per token); algorithmic bytes count each operand once."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from fine_grained_moe_amd.synthetic import WORKLOADS, gemm_useful_flops
+    w = WORKLOADS["fwdbwd"]
+    total = sum(bench.gemm_launch_flops(w, n) for n in bench.Layer.GEMMS)
+    assert abs(total - gemm_useful_flops(w, True)) <= 1e-9 * total
+    assert abs(total - 3 * (w.K + w.S) * 6 * w.H * w.F * w.T) <= 1e-9 * total
+    # gate/up forward: x rows in, W1 once, act (2F) and h (F) out, bf16
+    rows = w.T * w.K
+    exp = 2 * (rows * w.H + w.E * 2 * w.F * w.H + rows * 3 * w.F)
+    assert bench.gemm_launch_bytes(w, "gate_up_fwd") == exp
