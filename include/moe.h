@@ -105,6 +105,10 @@ size_t moe_route_bwd_dense_workspace_bytes(int32_t T, int32_t H, int32_t E);
  * balance loss (moe_seq_balance_fwd / _bwd).
  * ws: device workspace of at least moe_route_workspace_bytes(H,E) bytes (the
  * router weight re-encoded for the matrix cores; rewritten by every call).
+ * x must be finite: the projection multiplies x by the exact three-part split
+ * of each weight, so an infinite input meets zero parts and gives NaN logits;
+ * a NaN key ranks below every other (such a token selects experts 0..K-1 with
+ * NaN weights).
  */
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K,
                        const uint16_t* x, const float* w_router, const float* bias,

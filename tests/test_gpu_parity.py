@@ -283,6 +283,34 @@ def test_empty_batch(M):
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
 
 
+def test_route_special_values(M):
+    """Tokens with a NaN input (every logit NaN, ranked lowest: experts 0..K-1
+    in index order, NaN weights), all-zero tokens (every score exactly 1/2, so
+    the bias alone decides), and with a zero bias too exact key ties (lower
+    index first)."""
+    T, H, E, K = 64, 128, 16, 4
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[0:4, 5] = np.nan
+    x[4:8] = 0.0
+    xg = torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+    x = P.to_np(xg)
+    wr = (rng.standard_normal((H, E)) * 0.1).astype(np.float32)
+    for b in ((rng.standard_normal(E) * 0.05).astype(np.float32), np.zeros(E, np.float32)):
+        idx, tw, ts = M.moe_route(xg, torch.from_numpy(wr).to(DEV), torch.from_numpy(b).to(DEV), K)
+        idx, tw, ts = P.to_np(idx), P.to_np(tw), P.to_np(ts)
+        ref = O.route(x, wr, b, K)
+        assert (idx[0:4] == np.arange(K)).all() and (ref["topk_idx"][0:4] == np.arange(K)).all()
+        assert np.isnan(tw[0:4]).all() and np.isnan(ref["topk_w"][0:4]).all()
+        assert np.array_equal(idx[4:8], ref["topk_idx"][4:8])
+        assert (ts[4:8] == 0.5).all() and np.array_equal(tw[4:8], ref["topk_w"][4:8])
+        if not b.any():
+            assert (idx[4:8] == np.arange(K)).all()
+        sub = {k: (v[8:] if isinstance(v, np.ndarray) and v.shape[:1] == (T,) else v)
+               for k, v in ref.items()}
+        P.check_route(idx[8:], tw[8:], ts[8:], sub, "special")
+
+
 # ---------------------------------------------------------------------------
 # full dots.llm1-shaped workloads (the benchmark's launch configuration)
 # ---------------------------------------------------------------------------
