@@ -64,7 +64,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fwdbwd", choices=["fwdbwd", "prefill", "skew", "decode"])
+    ap.add_argument("--workload", default="fwdbwd",
+                    choices=["fwdbwd", "prefill", "skew", "decode", "ep_shard"],
+                    help="ep_shard: the grouped expert products alone (fwd+bwd) at one GPU's "
+                         "share of an 8-way expert-parallel layer, 16 experts x 3072 rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the same batch the CPU oracle runs on")
@@ -263,12 +266,122 @@ def cpu_baseline(w, g, n_tokens):
                 seconds=dt)
 
 
+SHARD_GEMMS = ("gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad", "down_wgrad",
+               "gate_up_wgrad")
+
+
+def shard_main(args):
+    """The six routed grouped-GEMM launches of one fwd+bwd step at the
+    expert-parallel shard shape (rows already grouped by expert, as the
+    dispatch exchange delivers them)."""
+    import torch
+    from fine_grained_moe_amd import moe as M
+    from fine_grained_moe_amd.synthetic import EP_SHARD, Workload, generate_shard_torch
+    E, R, H, F = EP_SHARD["E"], EP_SHARD["rows"], EP_SHARD["H"], EP_SHARD["F"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = generate_shard_torch(dev, E, R, H, F, EP_SHARD["seed"])
+    A = M.moe_align()
+    i32 = torch.int32
+    offsets = torch.arange(E + 1, dtype=i32, device=dev) * R
+    counts = torch.full((E,), R, dtype=i32, device=dev)
+    tile_expert = (torch.arange(E * R // A, dtype=i32, device=dev) // (R // A)).to(i32)
+    seg = (offsets, counts, tile_expert)
+    bf = torch.bfloat16
+    act = torch.empty((E * R, 2 * F), dtype=bf, device=dev)
+    h = torch.empty((E * R, F), dtype=bf, device=dev)
+    y_rows = torch.empty((E * R, H), dtype=bf, device=dev)
+    dact = torch.empty_like(act)
+    dx_rows = torch.empty_like(g["x_rows"])
+    dw1 = torch.empty_like(g["w1"])
+    dw2 = torch.empty_like(g["w2"])
+    fns = {
+        "gate_up_fwd": lambda: M.moe_grouped_gate_up_fwd(g["x_rows"], g["w1"], *seg, act=act, h=h),
+        "down_fwd": lambda: M.moe_grouped_down_fwd(h, g["w2"], *seg, y_rows=y_rows),
+        "down_dgrad": lambda: M.moe_grouped_down_dgrad(g["w2"], act, g["dy_rows"], *seg, dact=dact),
+        "gate_up_dgrad": lambda: M.moe_grouped_gate_up_dgrad(g["w1"], dact, *seg, dx_rows=dx_rows),
+        "down_wgrad": lambda: M.moe_grouped_down_wgrad(g["dy_rows"], h, E, *seg, dw2=dw2),
+        "gate_up_wgrad": lambda: M.moe_grouped_gate_up_wgrad(dact, g["x_rows"], E, *seg, dw1=dw1),
+    }
+    for _ in range(args.warmup):
+        for n in SHARD_GEMMS:
+            fns[n]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in SHARD_GEMMS} for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        for n in SHARD_GEMMS:
+            evs[i][n][0].record()
+            fns[n]()
+            evs[i][n][1].record()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in SHARD_GEMMS}
+    # the shard's rows stand for T*K routed rows of the layer: T = E*R/K with K = 6
+    w = Workload("ep_shard", T=E * R // 6, H=H, E=E, K=6, S=0, F=F, seed=EP_SHARD["seed"])
+    fl = {n: gemm_launch_flops(w, n) for n in SHARD_GEMMS}
+    flops = sum(fl.values())
+    tflops = flops / (ms * 1e-3) / 1e12
+    dom = max(SHARD_GEMMS, key=lambda n: launch_ms[n])
+    achieved = fl[dom] / (launch_ms[dom] * 1e-3) / 1e12
+    out = {
+        "metric": "grouped expert GEMMs, useful TFLOP/s at the expert-parallel shard (fwd+bwd)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"grouped SwiGLU expert GEMMs fwd+bwd at one GPU's share of an "
+                                f"8-way expert-parallel dots.llm1 layer: {E} experts x {R} rows, "
+                                f"H={H}, F={F}"), "E": E, "rows_per_expert": R, "H": H, "F": F},
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": f"grouped GEMM {dom}", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "launch_ms": round(launch_ms[dom], 4),
+                     "algorithmic_gb": round(gemm_launch_bytes(w, dom) / 1e9, 3), "traffic": None},
+        "gemm_launches": {n: {"ms": round(launch_ms[n], 4),
+                              "tflops": round(fl[n] / (launch_ms[n] * 1e-3) / 1e12, 1)}
+                          for n in SHARD_GEMMS},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = shard_cpu_baseline(g, R, F, w, n_experts=8)
+    print(json.dumps(out), flush=True)
+
+
+def shard_cpu_baseline(g, R, F, w, n_experts):
+    """The oracle's expert forward and backward on all rows of the first
+    n_experts experts of the shard (same unit: useful TFLOP/s)."""
+    import torch
+    from oracle import moe_oracle as O
+    dt = 0.0
+    for e in range(n_experts):
+        x = g["x_rows"][e * R:(e + 1) * R].float().cpu().numpy()
+        w1 = g["w1"][e].float().cpu().numpy()
+        w2 = g["w2"][e].float().cpu().numpy()
+        dy = g["dy_rows"][e * R:(e + 1) * R].float().cpu().numpy()
+        t0 = time.perf_counter()
+        a, _, _ = O.expert_ffn(x, w1, w2)
+        O.expert_ffn_bwd(x, w1, w2, a, dy)
+        dt += time.perf_counter() - t0
+    flops = 18.0 * n_experts * R * w.H * F
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle", seconds=dt,
+                sample=(f"fp64 NumPy oracle, forward+backward of {n_experts} of the {w.E} experts "
+                        f"(all {R} rows each), {dt:.1f} s; BLAS threads {torch.get_num_threads()}"))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the layer's multi-GPU "
               "sharding (expert parallel all-to-all) is not built", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "ep_shard":
+        return shard_main(args)
     import torch
     from fine_grained_moe_amd import moe as M
     from fine_grained_moe_amd.synthetic import WORKLOADS, generate_torch, useful_flops, gemm_useful_flops

@@ -182,6 +182,42 @@ def generate_torch(w: Workload, device, with_dy: bool | None = None) -> dict:
     return out
 
 
+# ----------------------------------------------------------------------------
+# The expert-parallel shard (one GPU's share when the layer is split over 8)
+# ----------------------------------------------------------------------------
+# With expert parallelism over 8 GPUs each GPU holds 16 of the 128 routed
+# experts and receives, through the dispatch exchange, the rows its experts
+# were picked for: 8 GPUs x 8192 tokens x 6 picks / 128 experts = 3072 rows
+# per expert at near-uniform routing ("dots.llm1 Technical Report" summary,
+# "Method": expert-parallel training with the all-to-all overlapped).
+EP_SHARD = dict(E=16, rows=3072, H=5120, F=1408, seed=5)
+
+
+def generate_shard_torch(device, E: int, rows: int, H: int, F: int, seed: int) -> dict:
+    """Inputs of the grouped expert products at the shard, drawn on `device`
+    in the order x_rows, w1, w2, dy_rows (bf16): x_rows [E*rows, H] ~ N(0,1)
+    (the received rows, grouped by expert), w1 [E, 2F, H] and w2 [E, H, F]
+    ~ N(0, 0.02), dy_rows [E*rows, H] ~ N(0,1) (the returned gradient rows)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def normal(shape, std):
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+                * std).to(torch.bfloat16)
+
+    x_rows = normal((E * rows, H), 1.0)
+    w1 = torch.empty((E, 2 * F, H), dtype=torch.bfloat16, device=device)
+    for e in range(E):
+        w1[e] = normal((2 * F, H), 0.02)
+    w2 = torch.empty((E, H, F), dtype=torch.bfloat16, device=device)
+    for e in range(E):
+        w2[e] = normal((H, F), 0.02)
+    dy_rows = normal((E * rows, H), 1.0)
+    return dict(x_rows=x_rows, w1=w1, w2=w2, dy_rows=dy_rows)
+
+
 def useful_flops(w: Workload, backward: bool) -> float:
     """Algorithmic flops of the layer, padding rows excluded.
 

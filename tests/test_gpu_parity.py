@@ -11,7 +11,8 @@ import os
 import numpy as np
 import pytest
 
-from fine_grained_moe_amd.synthetic import WORKLOADS, Workload, generate_numpy, generate_torch
+from fine_grained_moe_amd.synthetic import (EP_SHARD, WORKLOADS, Workload, generate_numpy,
+                                            generate_shard_torch, generate_torch)
 from oracle import moe_oracle as O
 import parity as P
 
@@ -429,3 +430,50 @@ def test_skew_sampled(M):
 @pytest.mark.timeout(600)
 def test_fwdbwd_sampled(M):
     sampled_checks(M, WORKLOADS["fwdbwd"], backward=True)
+
+
+@pytest.mark.timeout(600)
+def test_ep_shard_sampled(M):
+    """The six routed grouped products at one GPU's share of an 8-way
+    expert-parallel layer (16 experts x 3072 rows, the benchmark's ep_shard
+    configuration): sampled rows of sampled experts stage by stage, and the
+    weight gradients of sampled hidden units over all of the expert's rows."""
+    E, R, H, F = EP_SHARD["E"], EP_SHARD["rows"], EP_SHARD["H"], EP_SHARD["F"]
+    g = generate_shard_torch(DEV, E, R, H, F, EP_SHARD["seed"])
+    i32 = torch.int32
+    offsets = torch.arange(E + 1, dtype=i32, device=DEV) * R
+    counts = torch.full((E,), R, dtype=i32, device=DEV)
+    tile_expert = (torch.arange(E * R // ALIGN, dtype=i32, device=DEV) // (R // ALIGN)).to(i32)
+    seg = (offsets, counts, tile_expert)
+    act, h = M.moe_grouped_gate_up_fwd(g["x_rows"], g["w1"], *seg)
+    y_rows = M.moe_grouped_down_fwd(h, g["w2"], *seg)
+    dact = M.moe_grouped_down_dgrad(g["w2"], act, g["dy_rows"], *seg)
+    dx_rows = M.moe_grouped_gate_up_dgrad(g["w1"], dact, *seg)
+    dw2 = M.moe_grouped_down_wgrad(g["dy_rows"], h, E, *seg)
+    dw1 = M.moe_grouped_gate_up_wgrad(dact, g["x_rows"], E, *seg)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    W1, W2 = LazyExperts(g["w1"]), LazyExperts(g["w2"])
+    for e in (0, 9, E - 1):
+        rows = np.sort(rng.choice(R, 256, replace=False)) + e * R
+        sel = torch.from_numpy(rows).to(DEV)
+        xr = P.to_np(g["x_rows"][sel])
+        a, hid, ye = O.expert_ffn(xr, W1[e], W2[e])
+        P.assert_close(f"shard act[e={e}]", P.to_np(act[sel]), a)
+        P.assert_close(f"shard h[e={e}]", P.to_np(h[sel]), hid)
+        P.assert_close(f"shard y_rows[e={e}]", P.to_np(y_rows[sel]), ye)
+        dxr, _, _, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, P.to_np(g["dy_rows"][sel]))
+        P.assert_close(f"shard dact[e={e}]", P.to_np(dact[sel]), dar)
+        P.assert_close(f"shard dx_rows[e={e}]", P.to_np(dx_rows[sel]), dxr)
+        # weight gradients of sampled hidden units over all of the expert's rows
+        all_rows = torch.arange(e * R, (e + 1) * R, device=DEV)
+        xa = P.to_np(g["x_rows"][all_rows])
+        dya = P.to_np(g["dy_rows"][all_rows])
+        for f in rng.choice(F, 2, replace=False):
+            w1u = W1[e][[f, F + f]]
+            w2u = W2[e][:, [f]]
+            au, _, _ = O.expert_ffn(xa, w1u, w2u)
+            _, dw1u, dw2u, _ = O.expert_ffn_bwd(xa, w1u, w2u, au, dya)
+            P.assert_close(f"shard dW1[{e},{f}] gate", P.to_np(dw1[e, f]), dw1u[0])
+            P.assert_close(f"shard dW1[{e},{f}] up", P.to_np(dw1[e, F + f]), dw1u[1])
+            P.assert_close(f"shard dW2[{e}][:,{f}]", P.to_np(dw2[e][:, f]), dw2u[:, 0])
