@@ -76,25 +76,9 @@ struct TileCfg {
 #ifndef MOE_WIDE_STAGES
 #define MOE_WIDE_STAGES 4
 #endif
-// row-grouped tile order: 1 = expert-major (all m-tiles of one expert and one
-// n-tile adjacent, then the next n-tile of the same expert); 0 = groups of
-// GROUP_M m-tiles regardless of expert boundaries
-#ifndef MOE_EXPERT_MAJOR
-#define MOE_EXPERT_MAJOR 1
-#endif
-#ifndef MOE_ROWS_WGM
-#define MOE_ROWS_WGM 2
-#endif
-#ifndef MOE_ROWS_WGN
-#define MOE_ROWS_WGN 4
-#endif
-#ifndef MOE_ROWS_MINB
-#define MOE_ROWS_MINB 1
-#endif
-// 128 x 256 row tiles; default 8 waves (wave tile 64 x 64), one workgroup per CU,
+// 128 x 256 row tiles, 8 waves (wave tile 64 x 64), one workgroup per CU,
 // 64-deep k stages (128-byte row segments per load)
-using CfgRows =
-    TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, MOE_ROWS_WGM, MOE_ROWS_WGN, MOE_ROWS_MINB>;
+using CfgRows = TileCfg<128, 256, MOE_ROWS_BK, MOE_ROWS_STAGES, 2, 4, 1>;
 // 128 x 512 row tiles, 8 waves of 64 x 128, four 32-deep stages (160 KB):
 // the gate/up data gradient (N = H, B N-contig), where the wider wave tile
 // halves the B fragment reads per MFMA and measured 7 % faster than CfgRows
@@ -108,7 +92,7 @@ using CfgWide = TileCfg<256, 256, MOE_WIDE_BK, MOE_WIDE_STAGES, 2, 4, 1>;
 using CfgWgrad = CfgWide;
 static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
 
-constexpr int GROUP_M = 4;  // m-tiles per rasterization group (row-grouped, non-expert-major)
+constexpr int GROUP_M = 4;  // m-tiles per rasterization group (dense row products)
 // K-grouped weight gradients: m-tiles per rasterization group inside one
 // expert, so a column slab of the second operand is reused by several m-tiles
 // while it is resident in L2
@@ -252,7 +236,7 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   if constexpr (MODE == MGROUP) {
     if (a.tile_expert == nullptr) {
       e = 0;
-    } else if (MOE_EXPERT_MAJOR) {
+    } else {
       // tiles of expert e occupy [n_ntiles * mstart_e, n_ntiles * mend_e) in
       // the logical order, m-tile fastest, so the m-tiles sharing one weight
       // slice are adjacent and an expert's rows stay hot across its n-tiles
@@ -264,9 +248,6 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
       const int local = L - a.n_ntiles * mstart;
       mt = mstart + local % me;
       nt = local / me;
-    } else {
-      e = a.tile_expert[mt];
-      if (e < 0) return;
     }
   }
 
