@@ -35,14 +35,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "91e714d91f315951e8409c651c0e33a13fa79ba80249cc42d72984f153664ff7"
+TRAFFIC_SOURCE_SHA256 = "90e2cdce45d1788b0e52b9f0c112d75400c9b74c8e69abd2712d4f2627a9c266"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3089712.0, 405504.0), "down_fwd": (1143370.8, 491520.0),
+    "gate_up_fwd": (3095284.9, 405504.0), "down_fwd": (1142610.0, 491520.0),
     "shared_gate_up_fwd": (348240.3, 135168.0), "shared_down_fwd": (180294.3, 81920.0),
-    "down_dgrad": (1881249.8, 270336.0), "gate_up_dgrad": (2585312.8, 491520.0),
-    "down_wgrad": (594303.3, 1802240.0), "gate_up_wgrad": (1095768.1, 3604480.0),
-    "shared_down_dgrad": (352382.0, 90112.0), "shared_gate_up_dgrad": (360522.4, 81920.0),
-    "shared_down_wgrad": (217162.8, 28160.0), "shared_gate_up_wgrad": (434252.2, 56320.0),
+    "down_dgrad": (1891665.8, 270336.0), "gate_up_dgrad": (2606149.1, 491520.0),
+    "down_wgrad": (588862.8, 1802240.0), "gate_up_wgrad": (1101126.1, 3604480.0),
+    "shared_down_dgrad": (352605.4, 90112.0), "shared_gate_up_dgrad": (360522.6, 81920.0),
+    "shared_down_wgrad": (217162.8, 28160.0), "shared_gate_up_wgrad": (434252.1, 56320.0),
 }
 
 
