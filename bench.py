@@ -102,7 +102,7 @@ class Layer:
             perm=dict(counts=e(E, dt=i32), offsets=e(E + 1, dt=i32), row_of=e(T, K, dt=i32),
                       src_token=e(m_cap, dt=i32), tile_expert=e(m_cap // A, dt=i32),
                       x_rows=e(m_cap, H)),
-            route_ws=e(M.moe_route_workspace_bytes(H, E), dt=torch.uint8),
+            route_ws=e(M.moe_route_workspace_bytes(T, H, E), dt=torch.uint8),
             perm_ws=e(max(M.moe_permute_workspace_bytes(T, E, K), 1), dt=torch.uint8),
             act=e(m_cap, 2 * F), h=e(m_cap, F), y_rows=e(m_cap, H),
             act_sh=e(T, 2 * SF), h_sh=e(T, SF), y_sh=e(T, H), y=e(T, H),

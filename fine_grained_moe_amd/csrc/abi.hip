@@ -66,9 +66,9 @@ int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K) {
   return capacity(T, E, K);
 }
 
-size_t moe_route_workspace_bytes(int32_t H, int32_t E) {
-  if (H <= 0 || E <= 0 || E > 128) return 0;
-  return moe::route_workspace_bytes(H, E);
+size_t moe_route_workspace_bytes(int32_t T, int32_t H, int32_t E) {
+  if (T < 0 || H <= 0 || H % 64 != 0 || E <= 0 || E > 128) return 0;
+  return moe::route_workspace_bytes(T, H, E);
 }
 
 size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
@@ -100,7 +100,7 @@ moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_
   if (st) return st;
   if (T == 0) return MOE_OK;
   REQUIRE(x && w_router && bias && topk_idx && topk_w, MOE_ERR_INVALID_ARGUMENT, "null pointer");
-  REQUIRE(ws != nullptr && ws_bytes >= moe_route_workspace_bytes(H, E),
+  REQUIRE(ws != nullptr && ws_bytes >= moe_route_workspace_bytes(T, H, E),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   return hip_status(moe::launch_route(T, H, E, K, x, w_router, bias, topk_idx, topk_w, topk_s,
                                       scores, ws, (hipStream_t)stream),

@@ -8,7 +8,7 @@ namespace moe {
 
 constexpr int kAlign = 128;  // grouped-GEMM row tile = segment alignment
 
-size_t route_workspace_bytes(int H, int E);
+size_t route_workspace_bytes(int T, int H, int E);
 hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const float* w_router,
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
                         float* scores, void* ws, hipStream_t s);

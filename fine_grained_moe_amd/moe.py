@@ -27,7 +27,7 @@ _SIGS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_align": (_i32, []),
     "moe_capacity_rows": (_i64, [_i32, _i32, _i32]),
-    "moe_route_workspace_bytes": (_sz, [_i32, _i32]),
+    "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_seq_balance_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -105,8 +105,8 @@ def moe_capacity_rows(T: int, E: int, K: int) -> int:
     return int(_lib.moe_capacity_rows(T, E, K))
 
 
-def moe_route_workspace_bytes(H: int, E: int) -> int:
-    return int(_lib.moe_route_workspace_bytes(H, E))
+def moe_route_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(_lib.moe_route_workspace_bytes(T, H, E))
 
 
 def moe_permute_workspace_bytes(T: int, E: int, K: int) -> int:
@@ -139,7 +139,7 @@ def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=
     topk_w = torch.empty((T, K), dtype=F32, device=dev) if topk_w is None else topk_w
     topk_s = torch.empty((T, K), dtype=F32, device=dev) if topk_s is None else topk_s
     if ws is None:
-        ws = torch.empty(max(moe_route_workspace_bytes(H, E), 1), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(moe_route_workspace_bytes(T, H, E), 1), dtype=torch.uint8, device=dev)
     _check(_lib.moe_route(T, H, E, K, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                           _ptr(bias, F32, "bias"), _ptr(topk_idx, I32, "topk_idx"),
                           _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"),

@@ -69,9 +69,11 @@ int32_t moe_align(void);
  * (x_rows, act, h, y_rows, dy_rows, dact, dx_rows) have this many rows. */
 int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K);
 
-/* host: bytes of the workspace moe_route needs, 3 * ceil(E/32)*32 * H * 2
- * (0 for an invalid H or E). */
-size_t moe_route_workspace_bytes(int32_t H, int32_t E);
+/* host: bytes of the workspace moe_route needs for T tokens: the router
+ * weight's three bf16 parts (3 * ceil(E/32)*32 * H * 2 bytes, rounded up to
+ * 256) and the projection's per-slice logits (S * T * 128 * 4 bytes, where S,
+ * the number of slices of h, depends on T and H).  0 for invalid arguments. */
+size_t moe_route_workspace_bytes(int32_t T, int32_t H, int32_t E);
 
 /* host: bytes of the workspace moe_permute needs. */
 size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
@@ -103,8 +105,9 @@ size_t moe_route_bwd_dense_workspace_bytes(int32_t T, int32_t H, int32_t E);
  * topk_idx [T,K] int32; topk_w [T,K] fp32; topk_s [T,K] fp32 (nullable);
  * scores [T,E] fp32 (nullable): every s[t,e], the input of the sequence-wise
  * balance loss (moe_seq_balance_fwd / _bwd).
- * ws: device workspace of at least moe_route_workspace_bytes(H,E) bytes (the
- * router weight re-encoded for the matrix cores; rewritten by every call).
+ * ws: device workspace of at least moe_route_workspace_bytes(T,H,E) bytes (the
+ * router weight re-encoded for the matrix cores and the partial logits of
+ * each slice of h; rewritten by every call).
  * x must be finite: the projection multiplies x by the exact three-part split
  * of each weight, so an infinite input meets zero parts and gives NaN logits;
  * a NaN key ranks below every other (such a token selects experts 0..K-1 with

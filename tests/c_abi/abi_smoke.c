@@ -101,7 +101,7 @@ int main(void) {
   int32_t* idx = dalloc((size_t)T * K * 4);
   float* tw = dalloc((size_t)T * K * 4);
   float* ts = dalloc((size_t)T * K * 4);
-  const size_t rws = moe_route_workspace_bytes(H, E), pws = moe_permute_workspace_bytes(T, E, K);
+  const size_t rws = moe_route_workspace_bytes(T, H, E), pws = moe_permute_workspace_bytes(T, E, K);
   void* rw = dalloc(rws);
   void* pw = dalloc(pws);
   int32_t* counts = dalloc((size_t)E * 4);

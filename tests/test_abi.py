@@ -54,9 +54,18 @@ def test_host_queries(lib):
     assert lib.moe_capacity_rows(256, 128, 6) == 17792
     assert lib.moe_capacity_rows(0, 8, 2) == 1024
     assert lib.moe_capacity_rows(-1, 8, 2) == -1
-    assert lib.moe_route_workspace_bytes(5120, 128) == 3 * 128 * 5120 * 2
-    assert lib.moe_route_workspace_bytes(64, 8) == 3 * 32 * 64 * 2
-    assert lib.moe_route_workspace_bytes(64, 0) == 0
+    # weight parts (3 x 32*ceil(E/32) x H bf16) + S slices x T x 128 fp32 logits,
+    # S doubled while the grid of ceil(T/128) x S workgroups stays below 256 and
+    # H splits into whole 32-deep stages
+    parts = 3 * 128 * 5120 * 2
+    assert lib.moe_route_workspace_bytes(8192, 5120, 128) == parts + 4 * 8192 * 128 * 4
+    assert lib.moe_route_workspace_bytes(16384, 5120, 128) == parts + 2 * 16384 * 128 * 4
+    assert lib.moe_route_workspace_bytes(256, 5120, 128) == parts + 32 * 256 * 128 * 4
+    assert lib.moe_route_workspace_bytes(0, 5120, 128) == parts
+    assert lib.moe_route_workspace_bytes(128, 64, 8) == 3 * 32 * 64 * 2 + 2 * 128 * 128 * 4
+    assert lib.moe_route_workspace_bytes(128, 64, 0) == 0
+    assert lib.moe_route_workspace_bytes(128, 96, 8) == 0
+    assert lib.moe_route_workspace_bytes(-1, 64, 8) == 0
     assert lib.moe_permute_workspace_bytes(8192, 128, 6) == 2 * 32 * 128 * 4
     assert lib.moe_permute_workspace_bytes(0, 128, 6) == 0
     assert lib.moe_route_bwd_workspace_bytes(8192, 5120, 128, 6) == 128 * 5120 * 4 + 65408 * 4
