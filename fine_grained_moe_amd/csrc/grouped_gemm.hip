@@ -532,7 +532,10 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
         const int q = tid + (u0 + u) * Cfg::NT, r = q / CPR, c = q % CPR;
         const int64_t row = row0 + r;
         const int col = col0 + c * 8;
-        if (row < row_lim && col < col_lim) *(u32x4*)(gbase + row * ld + col) = v[u];
+        // non-temporal: the launch never reads its outputs back, so they
+        // stream out instead of displacing operand lines in the caches
+        if (row < row_lim && col < col_lim)
+          __builtin_nontemporal_store(v[u], (u32x4*)(gbase + row * ld + col));
       }
     }
   };
