@@ -35,14 +35,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "90e2cdce45d1788b0e52b9f0c112d75400c9b74c8e69abd2712d4f2627a9c266"
+TRAFFIC_SOURCE_SHA256 = "dd60b090cf2d5b9a543a4abe10275ceb9112f7fc2064409d1c3162685572bb78"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3095284.9, 405504.0), "down_fwd": (1142610.0, 491520.0),
-    "shared_gate_up_fwd": (348240.3, 135168.0), "shared_down_fwd": (180294.3, 81920.0),
-    "down_dgrad": (1891665.8, 270336.0), "gate_up_dgrad": (2606149.1, 491520.0),
-    "down_wgrad": (588862.8, 1802240.0), "gate_up_wgrad": (1101126.1, 3604480.0),
-    "shared_down_dgrad": (352605.4, 90112.0), "shared_gate_up_dgrad": (360522.6, 81920.0),
-    "shared_down_wgrad": (217162.8, 28160.0), "shared_gate_up_wgrad": (434252.1, 56320.0),
+    "gate_up_fwd": (3083725.6, 405504.0), "down_fwd": (1078282.0, 491522.2),
+    "shared_gate_up_fwd": (348240.3, 135212.0), "shared_down_fwd": (180294.3, 81957.0),
+    "down_dgrad": (1918326.4, 270336.0), "gate_up_dgrad": (2548380.5, 491523.6),
+    "down_wgrad": (321991.8, 1802297.8), "gate_up_wgrad": (846948.8, 3605149.0),
+    "shared_down_dgrad": (352412.4, 90129.5), "shared_gate_up_dgrad": (360522.3, 81921.3),
+    "shared_down_wgrad": (217162.8, 28160.5), "shared_gate_up_wgrad": (434252.0, 56320.9),
 }
 
 
@@ -57,6 +57,27 @@ def traffic_of(name, w):
     return {"traffic": round(gb, 3), "traffic_unit": "GB per launch",
             "traffic_read_gb": round(fk * COUNTER_FACTORS["FETCH_SIZE"] * 1024 / 1e9, 3),
             "traffic_write_gb": round(wk * COUNTER_FACTORS["WRITE_SIZE"] * 1024 / 1e9, 3)}
+
+
+def roofline_of(name, w, launch_ms, traffic=True):
+    """Roofline entry of one grouped-GEMM launch: MFMA-bound (useful TFLOP/s
+    against the bf16 peak) when its arithmetic intensity (useful flops per
+    algorithmic byte) is at or above the ridge, else HBM-bound (algorithmic
+    GB/s against 8 TB/s)."""
+    flops, nbytes = gemm_launch_flops(w, name), gemm_launch_bytes(w, name)
+    sec = launch_ms * 1e-3
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tf, gbs = flops / sec / 1e12, nbytes / sec / 1e9
+    if flops / nbytes >= ridge:
+        r = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    else:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4), "achieved_tflops": round(tf, 2)}
+    r.update({"kernel": f"grouped GEMM {name}", "launch_ms": round(launch_ms, 4),
+              "flop_per_byte": round(flops / nbytes, 1), "algorithmic_gb": round(nbytes / 1e9, 3)})
+    r.update(traffic_of(name, w) if traffic else {"traffic": None})
+    return r
 
 
 def parse():
@@ -328,7 +349,6 @@ def shard_main(args):
     flops = sum(fl.values())
     tflops = flops / (ms * 1e-3) / 1e12
     dom = max(SHARD_GEMMS, key=lambda n: launch_ms[n])
-    achieved = fl[dom] / (launch_ms[dom] * 1e-3) / 1e12
     out = {
         "metric": "grouped expert GEMMs, useful TFLOP/s at the expert-parallel shard (fwd+bwd)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -338,11 +358,7 @@ def shard_main(args):
                                 f"8-way expert-parallel dots.llm1 layer: {E} experts x {R} rows, "
                                 f"H={H}, F={F}"), "E": E, "rows_per_expert": R, "H": H, "F": F},
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": f"grouped GEMM {dom}", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "launch_ms": round(launch_ms[dom], 4),
-                     "algorithmic_gb": round(gemm_launch_bytes(w, dom) / 1e9, 3), "traffic": None},
+        "roofline": roofline_of(dom, w, launch_ms[dom], traffic=False),
         "gemm_launches": {n: {"ms": round(launch_ms[n], 4),
                               "tflops": round(fl[n] / (launch_ms[n] * 1e-3) / 1e12, 1)}
                           for n in SHARD_GEMMS},
@@ -478,7 +494,6 @@ def main():
     gemm_flops = gemm_useful_flops(w, backward)
     # the dominant kernel: the grouped-GEMM launch with the longest average time
     dom = max(names, key=lambda n: launch_ms[n])
-    achieved = gemm_launch_flops(w, dom) / (launch_ms[dom] * 1e-3) / 1e12
     counts = layer.b["perm"]["counts"].cpu().numpy()
     launches = {n: {"ms": round(launch_ms[n], 4),
                     "tflops": round(gemm_launch_flops(w, n) / (launch_ms[n] * 1e-3) / 1e12, 1),
@@ -508,12 +523,7 @@ def main():
         "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gemm_ms": round(gemm_ms, 4),
         "routed_nonempty_experts": int((counts > 0).sum()),
-        "roofline": {"kernel": f"grouped GEMM {dom}", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "launch_ms": round(launch_ms[dom], 4),
-                     "algorithmic_gb": round(gemm_launch_bytes(w, dom) / 1e9, 3),
-                     **traffic_of(dom, w)},
+        "roofline": roofline_of(dom, w, launch_ms[dom]),
         "gemm_launches": launches,
     }
     if bal is not None:

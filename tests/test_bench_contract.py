@@ -28,3 +28,22 @@ def test_gemm_flop_and_byte_accounting():
     rows = w.T * w.K
     exp = 2 * (rows * w.H + w.E * 2 * w.F * w.H + rows * 3 * w.F)
     assert bench.gemm_launch_bytes(w, "gate_up_fwd") == exp
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    """A launch below the ridge (2516.6 TFLOP/s / 8 TB/s = 315 flop/B) is
+    reported against HBM in GB/s, one above it against the bf16 MFMA peak."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from fine_grained_moe_amd.synthetic import WORKLOADS
+    dec = bench.roofline_of("gate_up_fwd", WORKLOADS["decode"], 0.65)
+    assert dec["bound"] == "hbm" and dec["unit"] == "GB/s" and dec["flop_per_byte"] < 315
+    nbytes = bench.gemm_launch_bytes(WORKLOADS["decode"], "gate_up_fwd")
+    assert abs(dec["achieved"] - nbytes / 0.65e-3 / 1e9) <= 0.1
+    assert abs(dec["frac"] - dec["achieved"] / 8000.0) <= 1e-4
+    big = bench.roofline_of("gate_up_wgrad", WORKLOADS["fwdbwd"], 2.0)
+    assert big["bound"] == "mfma" and big["unit"] == "TFLOP/s" and big["flop_per_byte"] >= 315
+    flops = bench.gemm_launch_flops(WORKLOADS["fwdbwd"], "gate_up_wgrad")
+    assert abs(big["achieved"] - flops / 2.0e-3 / 1e12) <= 0.01
+    # HBM bytes from the counters are reported only for the source they were taken on
+    assert (big["traffic"] is None) == (bench.traffic_of("gate_up_wgrad", WORKLOADS["fwdbwd"])["traffic"] is None)
