@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call, so a rejected call launches
 // nothing and touches no device state.
 #include <stdio.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -26,6 +27,19 @@ moe_status_t hip_status(hipError_t e, const char* fn) {
   do {                         \
     if (!(cond)) return fail(st, __func__, msg); \
   } while (0)
+
+// every device pointer is read or written with 16-byte vector accesses (rows
+// are multiples of 128 bytes, so a 16-byte aligned base aligns every row);
+// workspaces are carved into 256-byte aligned parts.  NULL passes.
+template <class... P>
+bool aligned(uintptr_t a, P... p) {
+  return ((((uintptr_t)p) % a == 0) && ...);
+}
+#define REQUIRE_ALIGNED(...)                                            \
+  REQUIRE(aligned(16, __VA_ARGS__), MOE_ERR_INVALID_ARGUMENT,           \
+          "device pointers must be 16-byte aligned")
+#define REQUIRE_WS_ALIGNED(ws) \
+  REQUIRE(aligned(256, ws), MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned")
 
 moe_status_t check_dims(const char* fn, int32_t T, int32_t H, int32_t E, int32_t K) {
   if (T < 0 || H <= 0 || E <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "T<0 or H,E,K<=0");
@@ -102,6 +116,8 @@ moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_
   REQUIRE(x && w_router && bias && topk_idx && topk_w, MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_workspace_bytes(T, H, E),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQUIRE_ALIGNED(x, w_router, bias, topk_idx, topk_w, topk_s, scores);
+  REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_route(T, H, E, K, x, w_router, bias, topk_idx, topk_w, topk_s,
                                       scores, ws, (hipStream_t)stream),
                     __func__);
@@ -122,6 +138,8 @@ moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t ali
   const size_t need = moe::permute_workspace_bytes(T, E);
   REQUIRE(ws_bytes >= need && (need == 0 || ws != nullptr), MOE_ERR_WORKSPACE_TOO_SMALL,
           "workspace too small");
+  REQUIRE_ALIGNED(topk_idx, x, counts, offsets, row_of, src_token, tile_expert, x_rows);
+  REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_permute(T, H, E, K, align, topk_idx, x, m_cap, counts, offsets,
                                         row_of, src_token, tile_expert, x_rows, ws,
                                         (hipStream_t)stream),
@@ -153,6 +171,7 @@ moe_status_t moe_grouped_swiglu_fwd(int32_t G, int64_t m_rows, int32_t H, int32_
   if (st) return st;
   if (m_rows == 0) return MOE_OK;
   REQUIRE(x_rows && w1 && w2 && h && y_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, x_rows, w1, w2, act, h, y_rows);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = moe::launch_gemm_gate_up(G, m_rows, H, F, offsets, counts, tile_expert, x_rows,
                                           w1, act, h, s);
@@ -170,6 +189,7 @@ moe_status_t moe_grouped_gate_up_fwd(int32_t G, int64_t m_rows, int32_t H, int32
   if (st) return st;
   if (m_rows == 0) return MOE_OK;
   REQUIRE(x_rows && w1 && h, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, x_rows, w1, act, h);
   return hip_status(moe::launch_gemm_gate_up(G, m_rows, H, F, offsets, counts, tile_expert,
                                              x_rows, w1, act, h, (hipStream_t)stream),
                     __func__);
@@ -183,6 +203,7 @@ moe_status_t moe_grouped_down_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t 
   if (st) return st;
   if (m_rows == 0) return MOE_OK;
   REQUIRE(h && w2 && y_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, h, w2, y_rows);
   return hip_status(moe::launch_gemm_down(G, m_rows, H, F, offsets, counts, tile_expert, h, w2,
                                           y_rows, (hipStream_t)stream),
                     __func__);
@@ -195,6 +216,7 @@ moe_status_t moe_combine(int32_t T, int32_t H, int32_t K, const uint16_t* y_rows
   REQUIRE(H % 64 == 0 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "H % 64 != 0 or K > 16");
   if (T == 0) return MOE_OK;
   REQUIRE(y_rows && row_of && topk_w && y, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(y_rows, row_of, topk_w, y_shared, y);
   return hip_status(moe::launch_combine(T, H, K, y_rows, row_of, topk_w, y_shared, y,
                                         (hipStream_t)stream),
                     __func__);
@@ -208,6 +230,7 @@ moe_status_t moe_combine_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dy
   if (T == 0) return MOE_OK;
   REQUIRE(dy && y_rows && row_of && topk_w && dy_rows && dg, MOE_ERR_INVALID_ARGUMENT,
           "null pointer");
+  REQUIRE_ALIGNED(dy, y_rows, row_of, topk_w, dy_rows, dg);
   return hip_status(moe::launch_combine_bwd(T, H, K, dy, y_rows, row_of, topk_w, dy_rows, dg,
                                             (hipStream_t)stream),
                     __func__);
@@ -224,6 +247,8 @@ moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_
   if (st) return st;
   REQUIRE(x_rows && w1 && w2 && act && h && dy_rows && dact && dx_rows && dw1 && dw2,
           MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, x_rows, w1, w2, act, h, dy_rows, dact, dx_rows,
+                  dw1, dw2);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (m_rows > 0) {
@@ -250,6 +275,7 @@ moe_status_t moe_grouped_down_dgrad(int32_t G, int64_t m_rows, int32_t H, int32_
   if (st) return st;
   if (m_rows == 0) return MOE_OK;
   REQUIRE(w2 && act && dy_rows && dact, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, w2, act, dy_rows, dact);
   return hip_status(moe::launch_gemm_dgrad_down(G, m_rows, H, F, offsets, counts, tile_expert,
                                                 dy_rows, w2, act, dact, (hipStream_t)stream),
                     __func__);
@@ -262,6 +288,7 @@ moe_status_t moe_grouped_down_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_
   moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
   if (st) return st;
   REQUIRE(dy_rows && h && dw2, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, dy_rows, h, dw2);
   return hip_status(moe::launch_gemm_wgrad_down(G, m_rows, H, F, offsets, counts, dy_rows, h, dw2,
                                                 (hipStream_t)stream),
                     __func__);
@@ -275,6 +302,7 @@ moe_status_t moe_grouped_gate_up_dgrad(int32_t G, int64_t m_rows, int32_t H, int
   if (st) return st;
   if (m_rows == 0) return MOE_OK;
   REQUIRE(w1 && dact && dx_rows, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, w1, dact, dx_rows);
   return hip_status(moe::launch_gemm_dgrad_up(G, m_rows, H, F, offsets, counts, tile_expert, dact,
                                               w1, dx_rows, (hipStream_t)stream),
                     __func__);
@@ -287,6 +315,7 @@ moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int
   moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
   if (st) return st;
   REQUIRE(dact && x_rows && dw1, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(offsets, counts, tile_expert, dact, x_rows, dw1);
   return hip_status(moe::launch_gemm_wgrad_up(G, m_rows, H, F, offsets, counts, dact, x_rows, dw1,
                                               (hipStream_t)stream),
                     __func__);
@@ -304,6 +333,9 @@ moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uin
           MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_workspace_bytes(T, H, E, K),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQUIRE_ALIGNED(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, dw_router,
+                  dx_router);
+  REQUIRE_WS_ALIGNED(ws);
   // T == 0 still writes the (zero) router weight gradient
   return hip_status(moe::launch_route_bwd(T, H, E, K, x_rows, w_router, topk_idx, topk_s, dg,
                                           row_of, offsets, counts, dw_router, dx_router, ws,
@@ -318,6 +350,7 @@ moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx
   REQUIRE(H % 64 == 0 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "H % 64 != 0 or K > 16");
   if (T == 0) return MOE_OK;
   REQUIRE(dx_rows && row_of && dx, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(dx_rows, row_of, dx_shared, dx_router, dx);
   return hip_status(moe::launch_unpermute_add(T, H, K, dx_rows, row_of, dx_shared, dx_router, dx,
                                               (hipStream_t)stream),
                     __func__);
@@ -328,6 +361,7 @@ moe_status_t moe_bias_update(int32_t E, const int32_t* counts, float* bias, floa
   REQUIRE(E > 0, MOE_ERR_INVALID_ARGUMENT, "E <= 0");
   REQUIRE(E <= 128, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128");
   REQUIRE(counts && bias, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(counts, bias);
   return hip_status(moe::launch_bias_update(E, counts, bias, gamma, (hipStream_t)stream),
                     __func__);
 }
@@ -351,6 +385,8 @@ moe_status_t moe_seq_balance_fwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
   REQUIRE(scores && topk_idx && loss && seq_f, MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE(ws != nullptr && ws_bytes >= moe_seq_balance_workspace_bytes(T, E, seq_len),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQUIRE_ALIGNED(scores, topk_idx, loss, seq_f);
+  REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_seq_balance_fwd(T, E, K, seq_len, scores, topk_idx, alpha, loss,
                                                 seq_f, ws, (hipStream_t)stream),
                     __func__);
@@ -362,6 +398,7 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
   moe_status_t st = check_seq(__func__, T, E, K, seq_len);
   if (st) return st;
   REQUIRE(scores && seq_f && dlogit, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(scores, seq_f, dloss, dlogit);
   return hip_status(moe::launch_seq_balance_bwd(T, E, seq_len, scores, seq_f, alpha, dloss,
                                                 dlogit, (hipStream_t)stream),
                     __func__);
@@ -376,10 +413,10 @@ moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t
   if (T == 0) return MOE_OK;
   REQUIRE(x && w_router && dlogit && dw_router && dx_router, MOE_ERR_INVALID_ARGUMENT,
           "null pointer");
-  REQUIRE(((uintptr_t)dx_router & 15) == 0 && ((uintptr_t)ws & 255) == 0,
-          MOE_ERR_INVALID_ARGUMENT, "dx_router must be 16-byte and ws 256-byte aligned");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_dense_workspace_bytes(T, H, E),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQUIRE_ALIGNED(x, w_router, dlogit, dw_router, dx_router);
+  REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_route_bwd_dense(T, H, E, x, w_router, dlogit, dw_router,
                                                 dx_router, ws, (hipStream_t)stream),
                     __func__);

@@ -17,6 +17,9 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless a comment says "host".  bf16 values
  *     are passed as uint16_t bit patterns.  Every array is dense row-major.
+ *   - Every device pointer is 16-byte aligned and every workspace 256-byte
+ *     aligned (the kernels move rows with 16-byte vector accesses); a call
+ *     with a misaligned pointer is rejected with MOE_ERR_INVALID_ARGUMENT.
  *   - The caller owns every buffer.  The library never allocates device
  *     memory on these paths, never frees, and keeps no pointer after return.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the

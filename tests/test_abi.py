@@ -202,3 +202,28 @@ def test_balance_rejects(lib):
     assert lib.moe_seq_balance_workspace_bytes(8192, 128, 4096) > 0
     assert lib.moe_seq_balance_workspace_bytes(8192, 128, 3000) == 0
     assert lib.moe_route_bwd_dense_workspace_bytes(8192, 5120, 128) > 0
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Every device pointer must be 16-byte aligned and every workspace
+    256-byte aligned; the host check rejects the call before any launch."""
+    big = 1 << 30
+    f = lib.moe_route
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]
+    ok = [_p(FAKE)] * 7
+    assert f(8, 64, 8, 2, _p(FAKE + 8), *ok[1:], _p(FAKE), big, _p(None)) == 1   # x
+    assert f(8, 64, 8, 2, *ok[:6], _p(FAKE + 4), _p(FAKE), big, _p(None)) == 1   # scores
+    assert f(8, 64, 8, 2, *ok, _p(FAKE + 16), big, _p(None)) == 1                # workspace
+    lib.moe_last_error.restype = ctypes.c_char_p
+    assert b"256-byte" in lib.moe_last_error()
+    g = lib.moe_grouped_gate_up_fwd
+    g.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 8
+    assert g(1, 128, 64, 32, _p(None), _p(None), _p(None), _p(FAKE), _p(FAKE + 2), _p(FAKE),
+             _p(FAKE), _p(None)) == 1                                              # w1
+    assert b"16-byte" in lib.moe_last_error()
+    c = lib.moe_combine
+    c.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
+    assert c(4, 64, 2, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE + 8), _p(FAKE), _p(None)) == 1  # y_shared
+    pb = lib.moe_permute_bwd
+    pb.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
+    assert pb(4, 64, 2, _p(FAKE), _p(FAKE), _p(None), _p(FAKE + 4), _p(FAKE), _p(None)) == 1  # dx_router
