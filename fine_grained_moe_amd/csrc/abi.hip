@@ -162,6 +162,17 @@ static moe_status_t check_grouped(const char* fn, int32_t G, int64_t m_rows, int
   return MOE_OK;
 }
 
+// The weight gradients address a whole segment (an expert's rows, or the m_rows
+// of a dense call) through one buffer resource with 32-bit byte offsets, so a
+// segment of rows of up to max(H, 2F) bf16 values must stay below 4 GiB.  No
+// segment holds more than m_rows rows.
+static moe_status_t check_wgrad_rows(const char* fn, int64_t m_rows, int32_t H, int32_t F) {
+  const int64_t row_bytes = 2 * (int64_t)(H > 2 * F ? H : 2 * F);
+  if (m_rows * row_bytes >= ((int64_t)1 << 32))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "m_rows * row bytes >= 4 GiB (weight-gradient segment)");
+  return MOE_OK;
+}
+
 moe_status_t moe_grouped_swiglu_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t F,
                                     const int32_t* offsets, const int32_t* counts,
                                     const int32_t* tile_expert, const uint16_t* x_rows,
@@ -245,6 +256,8 @@ moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_
                                     void* stream) {
   moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
   if (st) return st;
+  st = check_wgrad_rows(__func__, m_rows, H, F);
+  if (st) return st;
   REQUIRE(x_rows && w1 && w2 && act && h && dy_rows && dact && dx_rows && dw1 && dw2,
           MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE_ALIGNED(offsets, counts, tile_expert, x_rows, w1, w2, act, h, dy_rows, dact, dx_rows,
@@ -287,6 +300,8 @@ moe_status_t moe_grouped_down_wgrad(int32_t G, int64_t m_rows, int32_t H, int32_
                                     const uint16_t* h, uint16_t* dw2, void* stream) {
   moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
   if (st) return st;
+  st = check_wgrad_rows(__func__, m_rows, H, F);
+  if (st) return st;
   REQUIRE(dy_rows && h && dw2, MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE_ALIGNED(offsets, counts, tile_expert, dy_rows, h, dw2);
   return hip_status(moe::launch_gemm_wgrad_down(G, m_rows, H, F, offsets, counts, dy_rows, h, dw2,
@@ -313,6 +328,8 @@ moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int
                                        const int32_t* tile_expert, const uint16_t* dact,
                                        const uint16_t* x_rows, uint16_t* dw1, void* stream) {
   moe_status_t st = check_grouped(__func__, G, m_rows, H, F, offsets, counts, tile_expert);
+  if (st) return st;
+  st = check_wgrad_rows(__func__, m_rows, H, F);
   if (st) return st;
   REQUIRE(dact && x_rows && dw1, MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE_ALIGNED(offsets, counts, tile_expert, dact, x_rows, dw1);
@@ -409,7 +426,9 @@ moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t
                                  float* dx_router, void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(T >= 0 && H > 0 && E > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,E<=0");
   REQUIRE(E <= 128 && H % 64 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128 or H % 64 != 0");
-  REQUIRE((int64_t)T * H < ((int64_t)1 << 40), MOE_ERR_UNSUPPORTED_SHAPE, "T*H too large");
+  // the weight gradient addresses each token slice of x with 32-bit offsets
+  REQUIRE(T == 0 || moe::route_bwd_dense_slice_rows(T, H, E) * H * 2 < ((int64_t)1 << 32),
+          MOE_ERR_UNSUPPORTED_SHAPE, "token slice of x >= 4 GiB");
   if (T == 0) return MOE_OK;
   REQUIRE(x && w_router && dlogit && dw_router && dx_router, MOE_ERR_INVALID_ARGUMENT,
           "null pointer");

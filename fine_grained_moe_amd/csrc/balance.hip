@@ -346,6 +346,11 @@ size_t route_bwd_dense_workspace_bytes(int T, int H, int E) {
   return bal::dense_ws(T, H, E, nullptr).bytes;
 }
 
+int64_t route_bwd_dense_slice_rows(int T, int H, int E) {
+  const int G = bal::dw_slices(T, H, (E + 7) / 8 * 8);
+  return ((int64_t)T + G - 1) / G;
+}
+
 hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const float* w_router,
                                   const float* dlogit, float* dw_router, float* dx_router,
                                   void* ws, hipStream_t s) {

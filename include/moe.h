@@ -30,7 +30,9 @@
  *   - Outputs are deterministic: the same inputs give bit-identical outputs
  *     (no floating-point atomics anywhere).
  *   - Shape limits: H % 64 == 0, F % 32 == 0, 1 <= K <= E <= 128, K <= 16,
- *     align == moe_align(); row counts below 2^31.
+ *     align == moe_align(); row counts below 2^31; for the weight-gradient
+ *     entry points m_rows * max(H, 2F) * 2 bytes below 4 GiB (each segment
+ *     is addressed with 32-bit offsets; 419,430 rows at H = 5120).
  *
  * Readings of what the pages leave open (all entry points follow them):
  *   scores are sigmoid(logit); the bias is added for selection only; the K
@@ -357,6 +359,9 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
  *   dw_router[h,e] += sum_t x[t,h] * dlogit[t,e]      (fp32 [H,E])
  *   dx_router[t,h] += sum_e dlogit[t,e] * w_router[h,e] (fp32 [T,H])
  * x [T,H] bf16 in token order; dlogit [T,E] fp32; dx_router 16-byte aligned.
+ * The weight gradient runs over token slices of x addressed with 32-bit
+ * offsets; T whose largest slice reaches 4 GiB (beyond about 5.4 million
+ * tokens at H = 5120, E = 128) is rejected with MOE_ERR_UNSUPPORTED_SHAPE.
  * The products run on the bf16 matrix cores with every fp32 operand split
  * exactly into three bf16 parts (fp32-level accuracy).  Every sum runs in a
  * fixed order.  ws: at least moe_route_bwd_dense_workspace_bytes(T,H,E) bytes,

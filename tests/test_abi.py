@@ -227,3 +227,22 @@ def test_misaligned_pointers_rejected(lib):
     pb = lib.moe_permute_bwd
     pb.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6
     assert pb(4, 64, 2, _p(FAKE), _p(FAKE), _p(None), _p(FAKE + 4), _p(FAKE), _p(None)) == 1  # dx_router
+
+
+def test_segments_beyond_32_bit_offsets_rejected(lib):
+    """Weight gradients address a whole segment with 32-bit byte offsets: m_rows
+    rows of max(H, 2F) bf16 values must stay below 4 GiB (419,430 rows at
+    H = 5120); the dense router gradient bounds its token slices the same way."""
+    for name in ("moe_grouped_down_wgrad", "moe_grouped_gate_up_wgrad"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 7
+        seg = [_p(FAKE)] * 3
+        assert f(128, 419456, 5120, 1408, *seg, _p(None), _p(None), _p(None), _p(None)) == 2
+        assert f(128, 419328, 5120, 1408, *seg, _p(None), _p(None), _p(None), _p(None)) == 1  # null
+    g = lib.moe_grouped_swiglu_bwd
+    g.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 14
+    assert g(128, 419456, 5120, 1408, *[_p(FAKE)] * 3, *[_p(None)] * 11) == 2
+    d = lib.moe_route_bwd_dense
+    d.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert d(6_000_000, 5120, 128, *[_p(None)] * 6, 0, _p(None)) == 2
+    assert d(5_000_000, 5120, 128, *[_p(None)] * 6, 0, _p(None)) == 1   # null pointers
