@@ -94,6 +94,8 @@ def parse():
                     help="tokens of the same batch the CPU oracle runs on")
     ap.add_argument("--no-balance", action="store_true",
                     help="skip the timing of the step with load balancing")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the step captured as one HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device to device (known HBM bytes, for scaling "
                          "hardware byte counters)")
@@ -453,6 +455,33 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
 
+    # the same step captured once as a HIP graph and replayed (every entry
+    # point only launches kernels on the stream, into preallocated buffers);
+    # context beside the eager time, which stays the metric because the
+    # per-launch events need eager launches
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = r0.elapsed_time(r1) / args.steps
+        del graph
+
     # the step with load balancing (balance loss forward/backward, its dense
     # router gradients, the bias step), and each of those launches
     bal = None
@@ -522,6 +551,7 @@ def main():
         "fwd_pct_of_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gemm_ms": round(gemm_ms, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "routed_nonempty_experts": int((counts > 0).sum()),
         "roofline": roofline_of(dom, w, launch_ms[dom]),
         "gemm_launches": launches,
