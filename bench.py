@@ -219,6 +219,61 @@ class Layer:
                 p["counts"], b["bias_train"], GAMMA))
 
 
+    def step_two_streams(self, side, backward=True):
+        """The same step (no load balancing) with the independent launches on a
+        second stream, joined back through events: the shared experts'
+        products beside the router, permute and routed forward, and beside the
+        routed backward the shared data gradients and all weight gradients
+        (each as soon as its inputs exist).  Results are bit-identical to
+        forward() + backward(); the launches share the card, so none of them
+        can be timed alone here."""
+        import torch
+        M, g, b, K, E = self.M, self.g, self.b, self.K, self.E
+        p = b["perm"]
+        seg = (p["offsets"], p["counts"], p["tile_expert"])
+        main = torch.cuda.current_stream()
+
+        def mark(s):
+            e = torch.cuda.Event()
+            e.record(s)
+            return e
+
+        side.wait_event(mark(main))
+        with torch.cuda.stream(side):
+            M.moe_grouped_gate_up_fwd(g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"])
+            M.moe_grouped_down_fwd(b["h_sh"], self.w2f, y_rows=b["y_sh"])
+            shared_fwd = mark(side)
+            if backward:
+                M.moe_grouped_down_dgrad(self.w2f, b["act_sh"], g["dy"], dact=b["dact_sh"])
+                M.moe_grouped_gate_up_dgrad(self.w1f, b["dact_sh"], dx_rows=b["dx_sh"])
+        M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
+                    ws=b["route_ws"])
+        M.moe_permute(b["topk_idx"], g["x"], E, out=p, ws=b["perm_ws"])
+        M.moe_grouped_gate_up_fwd(p["x_rows"], g["w1"], *seg, act=b["act"], h=b["h"])
+        M.moe_grouped_down_fwd(b["h"], g["w2"], *seg, y_rows=b["y_rows"])
+        main.wait_event(shared_fwd)
+        M.moe_combine(b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"])
+        if not backward:
+            main.wait_stream(side)
+            return
+        M.moe_combine_bwd(g["dy"], b["y_rows"], p["row_of"], b["topk_w"], dy_rows=b["dy_rows"],
+                          dg=b["dg"])
+        side.wait_event(mark(main))
+        with torch.cuda.stream(side):
+            M.moe_grouped_down_wgrad(b["dy_rows"], b["h"], E, *seg, dw2=b["dw2"])
+        M.moe_grouped_down_dgrad(g["w2"], b["act"], b["dy_rows"], *seg, dact=b["dact"])
+        side.wait_event(mark(main))
+        with torch.cuda.stream(side):
+            M.moe_grouped_gate_up_wgrad(b["dact"], p["x_rows"], E, *seg, dw1=b["dw1"])
+            M.moe_grouped_down_wgrad(g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"])
+            M.moe_grouped_gate_up_wgrad(b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"])
+        M.moe_grouped_gate_up_dgrad(g["w1"], b["dact"], *seg, dx_rows=b["dx_rows"])
+        M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
+                        p["offsets"], p["counts"], dw_router=b["dw_router"],
+                        dx_router=b["dx_router"], ws=b["rb_ws"])
+        main.wait_stream(side)
+        M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+
 def gemm_launch_flops(w, name):
     """Useful (padding-free) flops of one grouped-GEMM launch: 2*rows*N*K with
     rows = T*K routed rows, or T for the shared experts (one group of width S*F)."""
@@ -459,7 +514,7 @@ def main():
     # point only launches kernels on the stream, into preallocated buffers);
     # context beside the eager time, which stays the metric because the
     # per-launch events need eager launches
-    graph_ms = None
+    graph_ms = graph2_ms = None
     if not args.no_graph:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -480,6 +535,22 @@ def main():
         r1.record(stream)
         torch.cuda.synchronize()
         graph_ms = r0.elapsed_time(r1) / args.steps
+        del graph
+        # the two-stream schedule of the same step, captured the same way
+        side2 = torch.cuda.Stream()
+        layer.step_two_streams(side2, backward)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.step_two_streams(side2, backward)
+        graph.replay()
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        graph2_ms = r0.elapsed_time(r1) / args.steps
         del graph
 
     # the step with load balancing (balance loss forward/backward, its dense
@@ -552,6 +623,7 @@ def main():
         "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gemm_ms": round(gemm_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "graph_two_streams_ms_per_step": None if graph2_ms is None else round(graph2_ms, 4),
         "routed_nonempty_experts": int((counts > 0).sum()),
         "roofline": roofline_of(dom, w, launch_ms[dom]),
         "gemm_launches": launches,

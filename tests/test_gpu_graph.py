@@ -100,3 +100,46 @@ def test_step_graph_replays_match_eager(M, case):
         for n in ROWS:
             assert torch.equal(layer.b[n][valid], ref_rows[n]), f"{case}: replay {rep}: {n} rows differ"
     del graph
+
+
+def test_two_stream_step_matches_eager(M):
+    """The step with its independent launches on a second stream, eager and
+    captured as one graph (the streams become parallel branches), equals the
+    one-stream step bit for bit."""
+    import bench
+
+    w = Workload("graph-2s", T=1000, H=512, E=16, K=4, S=2, F=352, seed=32,
+                 router_std=0.08, bias_std=0.05)
+    dev = torch.device("cuda:0")
+    g = generate_torch(w, dev, with_dy=True)
+    layer = bench.Layer(M, g, w.K)
+    names = OUTPUTS
+    _step(layer, False)
+    torch.cuda.synchronize()
+    ref = {n: layer.b[n].clone() for n in names}
+    valid = layer.b["perm"]["src_token"] >= 0
+    ref_rows = {n: layer.b[n][valid].clone() for n in ROWS}
+
+    side = torch.cuda.Stream()
+    _scribble(layer.b, names + ROWS)
+    layer.step_two_streams(side)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(layer.b[n], ref[n]), f"two streams, eager: {n} differs"
+    for n in ROWS:
+        assert torch.equal(layer.b[n][valid], ref_rows[n]), f"two streams, eager: {n} rows differ"
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step_two_streams(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _scribble(layer.b, names + ROWS)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(layer.b[n], ref[n]), f"two streams, replay {rep}: {n} differs"
+        for n in ROWS:
+            assert torch.equal(layer.b[n][valid], ref_rows[n]), f"two streams, replay {rep}: {n} rows"
+    del graph
