@@ -26,7 +26,7 @@ PEAK_HBM_GBS = 8000.0
 # load balancing: sequences of 8192 tokens (the pre-training context length),
 # balance-loss coefficient and bias step (values of the DeepSeek recipe's order)
 SEQ_LEN, ALPHA, GAMMA = 8192, 1e-4, 1e-3
-BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_bwd_dense", "bias_update")
+BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense", "bias_update")
 
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
@@ -202,15 +202,20 @@ class Layer:
             g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"]))
         self._gemm("shared_gate_up_wgrad", ev, lambda: M.moe_grouped_gate_up_wgrad(
             b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"]))
-        M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
-                        p["offsets"], p["counts"], dw_router=b["dw_router"],
-                        dx_router=b["dx_router"], ws=b["rb_ws"])
-        if balance:
+        if not balance:
+            M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"],
+                            p["row_of"], p["offsets"], p["counts"], dw_router=b["dw_router"],
+                            dx_router=b["dx_router"], ws=b["rb_ws"])
+        else:
+            # the balance loss's dense logit gradient, the combine path's added
+            # into it, and one dense router backward for both
             self._gemm("seq_loss_bwd", ev, lambda: M.moe_seq_balance_bwd(
                 b["scores"], b["seq_f"], self.K, SEQ_LEN, ALPHA, b["dloss"], dlogit=b["dlogit_bal"]))
+            self._gemm("route_dlogit", ev, lambda: M.moe_route_dlogit(
+                b["topk_idx"], b["topk_s"], b["dg"], b["dlogit_bal"]))
             self._gemm("route_bwd_dense", ev, lambda: M.moe_route_bwd_dense(
                 g["x"], g["w_router"], b["dlogit_bal"], b["dw_router"], b["dx_router"],
-                ws=b["dense_ws"]))
+                ws=b["dense_ws"], accumulate=False))
         M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
         if balance:
             # the bias step on this batch's loads (a copy of the bias, so that

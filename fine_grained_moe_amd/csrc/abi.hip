@@ -421,15 +421,38 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
                     __func__);
 }
 
+moe_status_t moe_route_dlogit(int32_t T, int32_t E, int32_t K, const int32_t* topk_idx,
+                              const float* topk_s, const float* dg, float* dlogit, void* stream) {
+  REQUIRE(T >= 0 && E > 0 && K > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or E,K<=0");
+  REQUIRE(K <= E, MOE_ERR_INVALID_ARGUMENT, "K > E");
+  REQUIRE(E <= 128 && K <= 16, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128 or K > 16");
+  REQUIRE((int64_t)T * E < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED_SHAPE, "T*E too large");
+  if (T == 0) return MOE_OK;
+  REQUIRE(topk_idx && topk_s && dg && dlogit, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(topk_idx, topk_s, dg, dlogit);
+  return hip_status(moe::launch_route_dlogit(T, E, K, topk_idx, topk_s, dg, dlogit,
+                                             (hipStream_t)stream),
+                    __func__);
+}
+
 moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t* x,
                                  const float* w_router, const float* dlogit, float* dw_router,
-                                 float* dx_router, void* ws, size_t ws_bytes, void* stream) {
+                                 float* dx_router, int32_t accumulate, void* ws, size_t ws_bytes,
+                                 void* stream) {
   REQUIRE(T >= 0 && H > 0 && E > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,E<=0");
   REQUIRE(E <= 128 && H % 64 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128 or H % 64 != 0");
   // the weight gradient addresses each token slice of x with 32-bit offsets
   REQUIRE(T == 0 || moe::route_bwd_dense_slice_rows(T, H, E) * H * 2 < ((int64_t)1 << 32),
           MOE_ERR_UNSUPPORTED_SHAPE, "token slice of x >= 4 GiB");
-  if (T == 0) return MOE_OK;
+  if (T == 0) {
+    // nothing to add; written mode still leaves a (zero) weight gradient
+    if (accumulate) return MOE_OK;
+    REQUIRE(dw_router, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    REQUIRE_ALIGNED(dw_router);
+    return hip_status(moe::launch_route_bwd_dense(0, H, E, nullptr, nullptr, nullptr, dw_router,
+                                                  nullptr, false, nullptr, (hipStream_t)stream),
+                      __func__);
+  }
   REQUIRE(x && w_router && dlogit && dw_router && dx_router, MOE_ERR_INVALID_ARGUMENT,
           "null pointer");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_dense_workspace_bytes(T, H, E),
@@ -437,7 +460,8 @@ moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t
   REQUIRE_ALIGNED(x, w_router, dlogit, dw_router, dx_router);
   REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_route_bwd_dense(T, H, E, x, w_router, dlogit, dw_router,
-                                                dx_router, ws, (hipStream_t)stream),
+                                                dx_router, accumulate != 0, ws,
+                                                (hipStream_t)stream),
                     __func__);
 }
 

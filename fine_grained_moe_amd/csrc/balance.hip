@@ -1,6 +1,8 @@
 // Load balancing of the MoE router on gfx950: the auxiliary-loss-free bias
 // step, the sequence-wise balance loss (forward and backward), and the
-// router gradients of a dense logit gradient.
+// router gradients of a dense logit gradient (into which the combine path's
+// K-per-token logit gradient can first be added, so that one dense pass gives
+// the router gradients of both).
 //
 // dots.llm1 Technical Report summary, section "Method": load balancing by
 // DeepSeek's auxiliary-loss-free bias update, complemented by a sequence-wise
@@ -253,18 +255,44 @@ __global__ void seg_kernel(int G, int S, int T, int32_t* __restrict__ offsets,
 }
 
 // dW_r[h,e] += sum over slices g and parts p of part[g][h][p EP + e]
-__global__ void __launch_bounds__(256) dw_reduce_kernel(int H, int E, int EP, int G,
+__global__ void __launch_bounds__(256) dw_reduce_kernel(int H, int E, int EP, int G, int acc,
                                                         const float* __restrict__ part,
                                                         float* __restrict__ dw) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)H * E) return;
   const int64_t h = i / E;
   const int e = (int)(i % E);
-  float s = dw[i];
+  float s = acc ? dw[i] : 0.f;
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int p = 0; p < 3; ++p) s += part[((int64_t)g * H + h) * 3 * EP + p * EP + e];
   dw[i] = s;
+}
+
+// the combine path's logit gradient added into a dense [T,E] one: per token,
+// S = sum_j s_j, ds_k = (dg_k - sum_j s_j dg_j / S) / S and
+// dlogit[t, topk_idx[t,k]] += ds_k s_k (1 - s_k).  One thread per token; the K
+// experts of a token are distinct, so every entry has one writer.
+__global__ void __launch_bounds__(256) route_dlogit_kernel(int T, int E, int K,
+                                                           const int32_t* __restrict__ topk_idx,
+                                                           const float* __restrict__ topk_s,
+                                                           const float* __restrict__ dg,
+                                                           float* __restrict__ dlogit) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int64_t o = (int64_t)t * K;
+  float ssum = 0.f, sdg = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const float s = topk_s[o + k];
+    ssum += s;
+    sdg += s * dg[o + k];
+  }
+  for (int k = 0; k < K; ++k) {
+    const float s = topk_s[o + k];
+    const float ds = (dg[o + k] - sdg / ssum) / ssum;
+    float* d = dlogit + (int64_t)t * E + topk_idx[o + k];
+    *d += ds * s * (1.0f - s);
+  }
 }
 
 // token slices for dW_r: enough workgroups for the CUs (the grouped kernel
@@ -351,9 +379,23 @@ int64_t route_bwd_dense_slice_rows(int T, int H, int E) {
   return ((int64_t)T + G - 1) / G;
 }
 
+hipError_t launch_route_dlogit(int T, int E, int K, const int32_t* topk_idx, const float* topk_s,
+                               const float* dg, float* dlogit, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(bal::route_dlogit_kernel, dim3((T + 255) / 256), dim3(256), 0, s, T, E, K,
+                     topk_idx, topk_s, dg, dlogit);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const float* w_router,
                                   const float* dlogit, float* dw_router, float* dx_router,
-                                  void* ws, hipStream_t s) {
+                                  bool accumulate, void* ws, hipStream_t s) {
+  if (T == 0) {  // no tokens: the written weight gradient is zero
+    if (!accumulate)
+      hipLaunchKernelGGL(bal::dw_reduce_kernel, dim3((unsigned)(((int64_t)H * E + 255) / 256)),
+                         dim3(256), 0, s, H, E, E, 0, 0, (const float*)nullptr, dw_router);
+    return hipGetLastError();
+  }
   const int EP = (E + 7) / 8 * 8, G = bal::dw_slices(T, H, EP);
   const bal::DenseWs w = bal::dense_ws(T, H, E, ws);
   const int S = (T + G - 1) / G;
@@ -365,7 +407,7 @@ hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dx_r += [d parts] . [W_r parts]^T, K = 6 EP
-  e = launch_gemm_f32_nt(T, H, 6 * EP, w.a6, 6 * EP, w.w6, 6 * EP, dx_router, H, true, s);
+  e = launch_gemm_f32_nt(T, H, 6 * EP, w.a6, 6 * EP, w.w6, 6 * EP, dx_router, H, accumulate, s);
   if (e != hipSuccess) return e;
   // part[g] = x_g^T [d_hi | d_mid | d_lo]_g, then dW_r += the sum of the parts
   e = launch_gemm_f32_tn_grouped(G, w.offsets, w.counts, T, H, 3 * EP, x, H, w.d3, 3 * EP, w.part,
@@ -373,7 +415,7 @@ hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const 
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)H * E;
   hipLaunchKernelGGL(bal::dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, H,
-                     E, EP, G, w.part, dw_router);
+                     E, EP, G, accumulate ? 1 : 0, w.part, dw_router);
   return hipGetLastError();
 }
 

@@ -78,8 +78,10 @@ hipError_t launch_seq_balance_bwd(int T, int E, int L, const float* scores, cons
 size_t route_bwd_dense_workspace_bytes(int T, int H, int E);
 // rows of the largest token slice of the dense router weight gradient
 int64_t route_bwd_dense_slice_rows(int T, int H, int E);
+hipError_t launch_route_dlogit(int T, int E, int K, const int32_t* topk_idx, const float* topk_s,
+                               const float* dg, float* dlogit, hipStream_t s);
 hipError_t launch_route_bwd_dense(int T, int H, int E, const uint16_t* x, const float* w_router,
                                   const float* dlogit, float* dw_router, float* dx_router,
-                                  void* ws, hipStream_t s);
+                                  bool accumulate, void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -54,7 +54,8 @@ _SIGS = {
     "moe_seq_balance_fwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p, _sz,
                                    _p]),
     "moe_seq_balance_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p]),
-    "moe_route_bwd_dense": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_route_dlogit": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p]),
+    "moe_route_bwd_dense": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _sz, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -386,18 +387,36 @@ def moe_seq_balance_bwd(scores, seq_f, K, seq_len, alpha, dloss=None, dlogit=Non
     return dlogit
 
 
-def moe_route_bwd_dense(x, w_router, dlogit, dw_router, dx_router, ws=None):
-    """Adds the router gradients of a dense dlogit [T,E] into dw_router [H,E]
-    and dx_router [T,H] (both fp32, updated in place)."""
+def moe_route_dlogit(topk_idx, topk_s, dg, dlogit):
+    """Adds the combine path's logit gradient (K entries per token) into the
+    dense fp32 dlogit [T,E], in place; returns dlogit."""
+    T, K = topk_idx.shape
+    E = dlogit.shape[1]
+    _check(_lib.moe_route_dlogit(T, E, K, _ptr(topk_idx, I32, "topk_idx"),
+                                 _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
+                                 _ptr(dlogit, F32, "dlogit"), _stream()))
+    return dlogit
+
+
+def moe_route_bwd_dense(x, w_router, dlogit, dw_router=None, dx_router=None, ws=None,
+                        accumulate=True):
+    """Router gradients of a dense dlogit [T,E]: added into dw_router [H,E] and
+    dx_router [T,H] (fp32, in place) when accumulate, else written (then they
+    may be None and are allocated)."""
     T, H = x.shape
     E = w_router.shape[1]
+    if dw_router is None or dx_router is None:
+        if accumulate:
+            raise ValueError("accumulating needs dw_router and dx_router")
+        dw_router = torch.empty((H, E), dtype=F32, device=x.device) if dw_router is None else dw_router
+        dx_router = torch.empty((T, H), dtype=F32, device=x.device) if dx_router is None else dx_router
     if ws is None:
         ws = torch.empty(max(moe_route_bwd_dense_workspace_bytes(T, H, E), 1), dtype=torch.uint8,
                          device=x.device)
     _check(_lib.moe_route_bwd_dense(T, H, E, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                                     _ptr(dlogit, F32, "dlogit"), _ptr(dw_router, F32, "dw_router"),
-                                    _ptr(dx_router, F32, "dx_router"), _ptr(ws), ws.numel(),
-                                    _stream()))
+                                    _ptr(dx_router, F32, "dx_router"), 1 if accumulate else 0,
+                                    _ptr(ws), ws.numel(), _stream()))
     return dw_router, dx_router
 
 
@@ -454,15 +473,22 @@ def layer_backward(dy, ctx, dloss=None):
     if ctx["w1_shf"] is not None:
         _, dx_sh, dw1_sh, dw2_sh = moe_grouped_swiglu_bwd(ctx["x"], ctx["w1_shf"], ctx["w2_shf"],
                                                           ctx["act_sh"], ctx["h_sh"], dy)
-    dw_router, dx_router = moe_route_bwd(p["x_rows"], ctx["w_router"], ctx["topk_idx"],
-                                         ctx["topk_s"], dg, p["row_of"], p["offsets"], p["counts"])
-    dlogit_bal = None
-    if ctx.get("balance") is not None:
+    dlogit_bal = dlogit = None
+    if ctx.get("balance") is None:
+        dw_router, dx_router = moe_route_bwd(p["x_rows"], ctx["w_router"], ctx["topk_idx"],
+                                             ctx["topk_s"], dg, p["row_of"], p["offsets"],
+                                             p["counts"])
+    else:
+        # the balance loss's logit gradient is dense; the combine path's is
+        # added into (a copy of) it, and one dense router backward gives the
+        # router gradients of both
         alpha, seq_len = ctx["balance"]
         dlogit_bal = moe_seq_balance_bwd(ctx["scores"], ctx["seq_f"], ctx["topk_idx"].shape[1],
                                          seq_len, alpha, dloss)
-        moe_route_bwd_dense(ctx["x"], ctx["w_router"], dlogit_bal, dw_router, dx_router)
+        dlogit = moe_route_dlogit(ctx["topk_idx"], ctx["topk_s"], dg, dlogit_bal.clone())
+        dw_router, dx_router = moe_route_bwd_dense(ctx["x"], ctx["w_router"], dlogit,
+                                                   accumulate=False)
     dx = moe_permute_bwd(dx_rows, p["row_of"], dx_sh, dx_router)
     return dict(dx=dx, dw1=dw1, dw2=dw2, dw1_sh=dw1_sh, dw2_sh=dw2_sh, dw_router=dw_router,
                 dg=dg, dy_rows=dy_rows, dact=dact, dx_rows=dx_rows, dx_shared=dx_sh,
-                dx_router=dx_router, dlogit_balance=dlogit_bal)
+                dx_router=dx_router, dlogit_balance=dlogit_bal, dlogit=dlogit)

@@ -354,10 +354,25 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
                                  const float* dloss, float* dlogit, void* stream);
 
 /*
+ * moe_route_dlogit - the combine path's logit gradient (moe_route_bwd's, see
+ * there), ADDED into a dense logit gradient [T,E] fp32:
+ *   dlogit[t, topk_idx[t,k]] += ds[t,k] * s (1 - s),   s = topk_s[t,k]
+ * With the balance loss this folds the two logit gradients into one, and a
+ * single moe_route_bwd_dense (accumulate = 0) then gives the router weight and
+ * input gradients of both, in place of moe_route_bwd followed by
+ * moe_route_bwd_dense (accumulate = 1).  The K experts of a token are
+ * distinct, so every entry has one writer; T == 0 is a no-op.
+ */
+moe_status_t moe_route_dlogit(int32_t T, int32_t E, int32_t K, const int32_t* topk_idx,
+                              const float* topk_s, const float* dg, float* dlogit,
+                              void* stream);
+
+/*
  * moe_route_bwd_dense - router gradients of a dense logit gradient, ADDED to
- * the outputs (so it composes with moe_route_bwd, which writes them):
- *   dw_router[h,e] += sum_t x[t,h] * dlogit[t,e]      (fp32 [H,E])
- *   dx_router[t,h] += sum_e dlogit[t,e] * w_router[h,e] (fp32 [T,H])
+ * the outputs when accumulate != 0 (so it composes with moe_route_bwd, which
+ * writes them), written over them when accumulate == 0:
+ *   dw_router[h,e] (+)= sum_t x[t,h] * dlogit[t,e]      (fp32 [H,E])
+ *   dx_router[t,h] (+)= sum_e dlogit[t,e] * w_router[h,e] (fp32 [T,H])
  * x [T,H] bf16 in token order; dlogit [T,E] fp32; dx_router 16-byte aligned.
  * The weight gradient runs over token slices of x addressed with 32-bit
  * offsets; T whose largest slice reaches 4 GiB (beyond about 5.4 million
@@ -365,11 +380,13 @@ moe_status_t moe_seq_balance_bwd(int32_t T, int32_t E, int32_t K, int32_t seq_le
  * The products run on the bf16 matrix cores with every fp32 operand split
  * exactly into three bf16 parts (fp32-level accuracy).  Every sum runs in a
  * fixed order.  ws: at least moe_route_bwd_dense_workspace_bytes(T,H,E) bytes,
- * 256-byte aligned.
+ * 256-byte aligned.  T == 0 leaves the outputs as they are when accumulating
+ * and writes a zero dw_router otherwise.
  */
 moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t* x,
                                  const float* w_router, const float* dlogit, float* dw_router,
-                                 float* dx_router, void* ws, size_t ws_bytes, void* stream);
+                                 float* dx_router, int32_t accumulate, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

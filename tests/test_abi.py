@@ -190,12 +190,24 @@ def test_balance_rejects(lib):
     assert f(8, 8, 2, 4, _p(FAKE), _p(FAKE), 0.1, _p(None), _p(None), _p(None)) == 1  # null dlogit
 
     f = lib.moe_route_bwd_dense
-    f.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
-    assert f(8, 96, 8, *[_p(FAKE)] * 6, big, _p(None)) == 2      # H % 64
-    assert f(8, 64, 200, *[_p(FAKE)] * 6, big, _p(None)) == 2    # E > 128
-    assert f(8, 64, 8, *[_p(FAKE)] * 5, _p(None), big, _p(None)) == 3   # no workspace
-    assert f(8, 64, 8, *[_p(FAKE)] * 6, 4, _p(None)) == 3        # workspace too small
-    assert f(0, 64, 8, *[_p(None)] * 6, 0, _p(None)) == 0        # T = 0 no-op
+    # x, w_router, dlogit, dw_router, dx_router, accumulate, ws, ws_bytes, stream
+    f.argtypes = ([ctypes.c_int32] * 3 + [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p])
+    ok5 = [_p(FAKE)] * 5
+    assert f(8, 96, 8, *ok5, 1, _p(FAKE), big, _p(None)) == 2      # H % 64
+    assert f(8, 64, 200, *ok5, 1, _p(FAKE), big, _p(None)) == 2    # E > 128
+    assert f(8, 64, 8, *ok5, 1, _p(None), big, _p(None)) == 3      # no workspace
+    assert f(8, 64, 8, *ok5, 1, _p(FAKE), 4, _p(None)) == 3        # workspace too small
+    assert f(0, 64, 8, *[_p(None)] * 5, 1, _p(None), 0, _p(None)) == 0   # T = 0, adding: no-op
+    assert f(0, 64, 8, *[_p(None)] * 5, 0, _p(None), 0, _p(None)) == 1   # T = 0, writing: dw_router
+
+    f = lib.moe_route_dlogit
+    f.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 5
+    assert f(8, 8, 9, *[_p(FAKE)] * 4, _p(None)) == 1                # K > E
+    assert f(8, 200, 2, *[_p(FAKE)] * 4, _p(None)) == 2              # E > 128
+    assert f(8, 8, 2, _p(FAKE), _p(FAKE), _p(FAKE), _p(None), _p(None)) == 1   # null dlogit
+    assert f(8, 8, 2, _p(FAKE), _p(FAKE + 4), _p(FAKE), _p(FAKE), _p(None)) == 1  # misaligned
+    assert f(0, 8, 2, *[_p(None)] * 4, _p(None)) == 0                # T = 0 no-op
 
     lib.moe_seq_balance_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_route_bwd_dense_workspace_bytes.restype = ctypes.c_size_t
@@ -243,6 +255,7 @@ def test_segments_beyond_32_bit_offsets_rejected(lib):
     g.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 14
     assert g(128, 419456, 5120, 1408, *[_p(FAKE)] * 3, *[_p(None)] * 11) == 2
     d = lib.moe_route_bwd_dense
-    d.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
-    assert d(6_000_000, 5120, 128, *[_p(None)] * 6, 0, _p(None)) == 2
-    assert d(5_000_000, 5120, 128, *[_p(None)] * 6, 0, _p(None)) == 1   # null pointers
+    d.argtypes = ([ctypes.c_int32] * 3 + [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p])
+    assert d(6_000_000, 5120, 128, *[_p(None)] * 5, 1, _p(None), 0, _p(None)) == 2
+    assert d(5_000_000, 5120, 128, *[_p(None)] * 5, 1, _p(None), 0, _p(None)) == 1   # null pointers

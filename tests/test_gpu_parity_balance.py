@@ -7,7 +7,7 @@ input, as in the layer tests, so a near-tie flip cannot leak into them.
 import numpy as np
 import pytest
 
-from fine_grained_moe_amd.synthetic import Workload, generate_numpy
+from fine_grained_moe_amd.synthetic import WORKLOADS, Workload, generate_numpy, generate_torch
 from oracle import moe_oracle as O
 import parity as P
 
@@ -177,6 +177,78 @@ def test_route_bwd_dense(M, T, H, E):
                           dw_z, dx_z)
     P.assert_close(f"T{T} dW_r", P.to_np(dw_z), ref_dw, tol=1e-5, norm_tol=1e-6)
     P.assert_close(f"T{T} dx_r", P.to_np(dx_z), ref_dx, tol=1e-5, norm_tol=1e-6)
+    # written over whatever the outputs held (NaN here), not added
+    dw_n = torch.full((H, E), float("nan"), dtype=torch.float32, device=DEV)
+    dx_n = torch.full((T, H), float("nan"), dtype=torch.float32, device=DEV)
+    M.moe_route_bwd_dense(x_g, torch.from_numpy(w).to(DEV), torch.from_numpy(dl).to(DEV),
+                          dw_n, dx_n, accumulate=False)
+    assert torch.equal(dw_n, dw_z) and torch.equal(dx_n, dx_z), "written != added to zero"
+
+
+def test_route_bwd_dense_no_tokens(M):
+    """T = 0: adding leaves the outputs alone, writing gives a zero dW_r."""
+    H, E = 192, 48
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    w = torch.randn((H, E), device=DEV) * 0.02
+    dl = torch.empty((0, E), dtype=torch.float32, device=DEV)
+    dw = torch.full((H, E), 5.0, device=DEV)
+    dx = torch.empty((0, H), dtype=torch.float32, device=DEV)
+    M.moe_route_bwd_dense(x, w, dl, dw, dx)
+    torch.cuda.synchronize()
+    assert bool((dw == 5.0).all())
+    M.moe_route_bwd_dense(x, w, dl, dw, dx, accumulate=False)
+    torch.cuda.synchronize()
+    assert bool((dw == 0.0).all())
+
+
+# ---------------------------------------------------------------------------
+# the combine path's logit gradient added into a dense one, and the single
+# dense router backward that then replaces moe_route_bwd + moe_route_bwd_dense
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (300, 48, 3), (1000, 128, 6), (8192, 128, 6)])
+def test_route_dlogit(M, T, E, K):
+    rng = np.random.default_rng(7 * T + E + K)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)   # K distinct experts
+    ts = rng.uniform(0.05, 0.95, (T, K)).astype(np.float32)
+    dg = rng.standard_normal((T, K)).astype(np.float32)
+    base = (rng.standard_normal((T, E)) * 1e-3).astype(np.float32)
+    dl = torch.from_numpy(base).to(DEV)
+    M.moe_route_dlogit(torch.from_numpy(idx).to(DEV), torch.from_numpy(ts).to(DEV),
+                       torch.from_numpy(dg).to(DEV), dl)
+    H = 64
+    _, _, sparse = O.router_bwd(np.zeros((T, H), np.float32), np.zeros((H, E), np.float32), idx,
+                                ts, dg)
+    P.assert_close(f"T{T} dlogit (dense + routed)", P.to_np(dl), base + sparse, tol=1e-5,
+                   norm_tol=1e-6)
+    # entries no token selected are untouched
+    hit = np.zeros((T, E), bool)
+    np.put_along_axis(hit, idx.astype(np.int64), True, axis=1)
+    assert np.array_equal(P.to_np(dl)[~hit], base[~hit])
+
+
+def test_one_dense_router_backward_equals_sparse_plus_dense(M):
+    """At dots shapes on the GPU's own routing: moe_route_dlogit + one
+    moe_route_bwd_dense (written) gives the router gradients that moe_route_bwd
+    + moe_route_bwd_dense (added) give, to fp32 accuracy."""
+    w = WORKLOADS["fwdbwd"]
+    g = generate_torch(w, DEV)
+    idx, _, ts = M.moe_route(g["x"], g["w_router"], g["bias"], w.K)
+    p = M.moe_permute(idx, g["x"], w.E)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(71)
+    dg = torch.randn((w.T, w.K), generator=gen, device=DEV)
+    dl_bal = torch.randn((w.T, w.E), generator=gen, device=DEV) * 1e-4
+    dw_a, dx_a = M.moe_route_bwd(p["x_rows"], g["w_router"], idx, ts, dg, p["row_of"],
+                                 p["offsets"], p["counts"])
+    M.moe_route_bwd_dense(g["x"], g["w_router"], dl_bal, dw_a, dx_a)
+    dl = M.moe_route_dlogit(idx, ts, dg, dl_bal.clone())
+    dw_b, dx_b = M.moe_route_bwd_dense(g["x"], g["w_router"], dl, accumulate=False)
+    torch.cuda.synchronize()
+    for name, a, b in (("dW_r", dw_a, dw_b), ("dx_router", dx_a, dx_b)):
+        a, b = P.to_np(a).astype(np.float64), P.to_np(b).astype(np.float64)
+        err = np.abs(a - b).max() / np.abs(a).max()
+        print(f"{name}: max |fused - separate| / max = {err:.2e}", flush=True)
+        assert err <= 1e-5, name
 
 
 # ---------------------------------------------------------------------------
