@@ -37,12 +37,12 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "dd60b090cf2d5b9a543a4abe10275ceb9112f7fc2064409d1c3162685572bb78"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3083725.6, 405504.0), "down_fwd": (1078282.0, 491522.2),
-    "shared_gate_up_fwd": (348240.3, 135212.0), "shared_down_fwd": (180294.3, 81957.0),
-    "down_dgrad": (1918326.4, 270336.0), "gate_up_dgrad": (2548380.5, 491523.6),
-    "down_wgrad": (321991.8, 1802297.8), "gate_up_wgrad": (846948.8, 3605149.0),
-    "shared_down_dgrad": (352412.4, 90129.5), "shared_gate_up_dgrad": (360522.3, 81921.3),
-    "shared_down_wgrad": (217162.8, 28160.5), "shared_gate_up_wgrad": (434252.0, 56320.9),
+    "gate_up_fwd": (3092961.9, 405504.0), "down_fwd": (1085185.9, 491548.5),
+    "shared_gate_up_fwd": (348240.3, 135196.2), "shared_down_fwd": (180294.2, 81968.0),
+    "down_dgrad": (1924041.4, 270336.2), "gate_up_dgrad": (2562536.4, 491527.2),
+    "down_wgrad": (322354.3, 1802285.4), "gate_up_wgrad": (847620.0, 3605167.6),
+    "shared_down_dgrad": (352472.6, 90130.5), "shared_gate_up_dgrad": (360522.3, 81970.9),
+    "shared_down_wgrad": (217162.8, 28169.2), "shared_gate_up_wgrad": (434252.0, 56354.3),
 }
 
 
