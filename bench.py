@@ -322,9 +322,13 @@ class LazyExperts:
         return self.t[e].float().numpy()
 
 
-def cpu_baseline(w, g, n_tokens):
+def cpu_baseline(w, g, n_tokens, gpu=None):
     """The CPU oracle, untouched, on the first n_tokens tokens of the batch
-    (forward + backward).  Reported in the same unit (useful TFLOP/s)."""
+    (forward + backward).  Reported in the same unit (useful TFLOP/s).  With
+    `gpu` (the GPU step's y, dx and topk_idx of those tokens) it also reports
+    their agreement: routing (near-ties counted apart) and the max-norm
+    relative error ||g - r||_inf / ||r||_inf of y and dx on the tokens whose
+    routing agrees."""
     import torch
     from oracle import moe_oracle as O
     from fine_grained_moe_amd.synthetic import useful_flops
@@ -332,21 +336,33 @@ def cpu_baseline(w, g, n_tokens):
     sub = dict(x=tn(g["x"][:n_tokens]), w_router=tn(g["w_router"]), bias=tn(g["bias"]),
                w1=LazyExperts(g["w1"]), w2=LazyExperts(g["w2"]),
                w1_sh=tn(g["w1_sh"]), w2_sh=tn(g["w2_sh"]))
-    dy = tn(g["dy"][:n_tokens]) if "dy" in g else None
-    backward = dy is not None
+    backward = bool(w.backward) and "dy" in g   # the workload's own direction
+    dy = tn(g["dy"][:n_tokens]) if backward else None
     threads = torch.get_num_threads()
     t0 = time.perf_counter()
     fwd = O.forward(sub, w.K, 128)
-    if backward:
-        O.backward(sub, fwd, dy)
+    bwd = O.backward(sub, fwd, dy) if backward else None
     dt = time.perf_counter() - t0
     flops = useful_flops(w.with_(T=n_tokens), backward)
     cores = len(os.sched_getaffinity(0))
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
-                sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
-                        f"first {n_tokens} of the {w.T} tokens at the same shapes, one run, "
-                        f"{dt:.1f} s; BLAS threads {threads}"),
-                seconds=dt)
+    res = dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+               sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
+                       f"first {n_tokens} of the {w.T} tokens at the same shapes, one run, "
+                       f"{dt:.1f} s; BLAS threads {threads}"),
+               seconds=dt)
+    if gpu is not None:
+        tie = np.asarray(fwd["route"]["near_tie"], bool)
+        same = np.all(gpu["topk_idx"] == fwd["route"]["topk_idx"], axis=1)
+
+        def err(a, r):
+            return float(np.max(np.abs(a - r)) / np.max(np.abs(r)))
+        par = {"tokens": int(len(same)), "near_ties": int(tie.sum()),
+               "routing_differs_outside_near_ties": int((~same & ~tie).sum()),
+               "y_max_rel_err": err(gpu["y"][same], fwd["y"][same])}
+        if backward:
+            par["dx_max_rel_err"] = err(gpu["dx"][same], bwd["dx"][same])
+        res["parity"] = par
+    return res
 
 
 SHARD_GEMMS = ("gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad", "down_wgrad",
@@ -495,12 +511,17 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start.record(stream)
     for i in range(args.steps):
+        if i:
+            marks[i - 1].record(stream)
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
+    bounds = [t_start] + marks[:args.steps - 1] + [t_end]
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
     launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
     gemm_ms = sum(launch_ms.values())
 
@@ -612,6 +633,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -636,7 +659,17 @@ def main():
     if bal is not None:
         out["load_balancing"] = bal
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens)
+        # the plain step once more, so that y and dx hold its outputs (the
+        # balance loop changed dx); a token's y and dx depend on that token
+        # only, so the oracle's run on the first tokens checks them
+        step()
+        torch.cuda.synchronize()
+        n = min(args.cpu_tokens, w.T)
+        gpu = {"y": layer.b["y"][:n].float().cpu().numpy(),
+               "topk_idx": layer.b["topk_idx"][:n].cpu().numpy()}
+        if backward:
+            gpu["dx"] = layer.b["dx"][:n].float().cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens, gpu)
     print(json.dumps(out), flush=True)
 
 
