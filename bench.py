@@ -161,13 +161,15 @@ class Layer:
         M, g, b, K = self.M, self.g, self.b, self.K
         p = b["perm"]
         seg = (p["offsets"], p["counts"], p["tile_expert"])
-        M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
-                    ws=b["route_ws"], scores=b["scores"] if balance else None)
+        self._gemm("route", ev, lambda: M.moe_route(
+            g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
+            ws=b["route_ws"], scores=b["scores"] if balance else None))
         if balance:
             self._gemm("seq_loss_fwd", ev, lambda: M.moe_seq_balance_fwd(
                 b["scores"], b["topk_idx"], SEQ_LEN, ALPHA, loss=b["loss"], seq_f=b["seq_f"],
                 ws=b["seq_ws"]))
-        M.moe_permute(b["topk_idx"], g["x"], self.E, out=p, ws=b["perm_ws"])
+        self._gemm("permute", ev, lambda: M.moe_permute(
+            b["topk_idx"], g["x"], self.E, out=p, ws=b["perm_ws"]))
         self._gemm("gate_up_fwd", ev, lambda: M.moe_grouped_gate_up_fwd(
             p["x_rows"], g["w1"], *seg, act=b["act"], h=b["h"]))
         self._gemm("down_fwd", ev, lambda: M.moe_grouped_down_fwd(
@@ -176,14 +178,16 @@ class Layer:
             g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"]))
         self._gemm("shared_down_fwd", ev, lambda: M.moe_grouped_down_fwd(
             b["h_sh"], self.w2f, y_rows=b["y_sh"]))
-        M.moe_combine(b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"])
+        self._gemm("combine", ev, lambda: M.moe_combine(
+            b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"]))
 
     def backward(self, ev=None, balance=False):
         M, g, b = self.M, self.g, self.b
         p = b["perm"]
         seg = (p["offsets"], p["counts"], p["tile_expert"])
         E = self.E
-        M.moe_combine_bwd(g["dy"], b["y_rows"], p["row_of"], b["topk_w"], dy_rows=b["dy_rows"], dg=b["dg"])
+        self._gemm("combine_bwd", ev, lambda: M.moe_combine_bwd(
+            g["dy"], b["y_rows"], p["row_of"], b["topk_w"], dy_rows=b["dy_rows"], dg=b["dg"]))
         # routed experts: the four steps of moe_grouped_swiglu_bwd, one launch each
         self._gemm("down_dgrad", ev, lambda: M.moe_grouped_down_dgrad(
             g["w2"], b["act"], b["dy_rows"], *seg, dact=b["dact"]))
@@ -203,9 +207,10 @@ class Layer:
         self._gemm("shared_gate_up_wgrad", ev, lambda: M.moe_grouped_gate_up_wgrad(
             b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"]))
         if not balance:
-            M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"],
-                            p["row_of"], p["offsets"], p["counts"], dw_router=b["dw_router"],
-                            dx_router=b["dx_router"], ws=b["rb_ws"])
+            self._gemm("route_bwd", ev, lambda: M.moe_route_bwd(
+                p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
+                p["offsets"], p["counts"], dw_router=b["dw_router"], dx_router=b["dx_router"],
+                ws=b["rb_ws"]))
         else:
             # the balance loss's dense logit gradient, the combine path's added
             # into it, and one dense router backward for both
@@ -216,7 +221,8 @@ class Layer:
             self._gemm("route_bwd_dense", ev, lambda: M.moe_route_bwd_dense(
                 g["x"], g["w_router"], b["dlogit_bal"], b["dw_router"], b["dx_router"],
                 ws=b["dense_ws"], accumulate=False))
-        M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+        self._gemm("permute_bwd", ev, lambda: M.moe_permute_bwd(
+            b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"]))
         if balance:
             # the bias step on this batch's loads (a copy of the bias, so that
             # every timed step routes the same way)
@@ -278,6 +284,34 @@ class Layer:
                         dx_router=b["dx_router"], ws=b["rb_ws"])
         main.wait_stream(side)
         M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
+
+# the entry points around the grouped GEMMs, timed like them in the main loop
+ROW_OPS_FWD = ("route", "permute", "combine")
+ROW_OPS_BWD = ("combine_bwd", "route_bwd", "permute_bwd")
+
+
+def row_op_bytes(w, name):
+    """Algorithmic HBM bytes of one call of a routing / permutation / combine
+    entry point: each of its inputs read once and each output written once,
+    as the entry point takes and returns them (bf16 rows 2H bytes, fp32 rows
+    4H; index and weight arrays of T*K entries)."""
+    T, H, E, K = w.T, w.H, w.E, w.K
+    row, tk = 2 * H, T * K
+    if name == "route":        # x, W_r in; topk_idx / topk_w / topk_s out
+        return T * row + 4 * H * E + 12 * tk
+    if name == "permute":      # topk_idx, x in; x_rows (valid rows), row_of, src_token out
+        m_cap = ((tk + E * 127 + 127) // 128) * 128
+        return 4 * tk + T * row + tk * row + 4 * tk + 4 * m_cap
+    if name == "combine":      # y_rows, y_shared, row_of, topk_w in; y out
+        return tk * row + (T * row if w.S else 0) + 8 * tk + T * row
+    if name == "combine_bwd":  # dy, y_rows, row_of, topk_w in; dy_rows, dg out
+        return T * row + tk * row + 8 * tk + tk * row + 4 * tk
+    if name == "route_bwd":    # x_rows, W_r, topk_idx/s, dg, row_of in; dW_r, dx_router out
+        return tk * row + 4 * H * E + 16 * tk + 4 * H * E + 4 * T * H
+    if name == "permute_bwd":  # dx_rows, dx_shared, dx_router, row_of in; dx out
+        return tk * row + (T * row if w.S else 0) + 4 * T * H + 4 * tk + T * row
+    raise KeyError(name)
+
 
 def gemm_launch_flops(w, name):
     """Useful (padding-free) flops of one grouped-GEMM launch: 2*rows*N*K with
@@ -506,8 +540,9 @@ def main():
 
     # timed region: K whole steps; events inside bracket every grouped-GEMM launch
     names = Layer.GEMMS if backward else Layer.GEMMS[:4]
+    row_names = ROW_OPS_FWD + (ROW_OPS_BWD if backward else ())
     evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for n in names} for _ in range(args.steps)]
+            for n in names + row_names} for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -524,6 +559,8 @@ def main():
     step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
     launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
     gemm_ms = sum(launch_ms.values())
+    row_us = {n: 1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs]))
+              for n in row_names}
 
     # forward alone, timed the same way
     torch.cuda.synchronize()
@@ -655,6 +692,14 @@ def main():
         "routed_nonempty_experts": int((counts > 0).sum()),
         "roofline": roofline_of(dom, w, launch_ms[dom]),
         "gemm_launches": launches,
+        # routing, permutation and combine: algorithmic bytes (every input read
+        # once, every output written once) over the call's time, against 8 TB/s
+        "row_ops": {n: {"us": round(row_us[n], 2),
+                        "algorithmic_gb": round(row_op_bytes(w, n) / 1e9, 4),
+                        "gbs": round(row_op_bytes(w, n) / (row_us[n] * 1e-6) / 1e9, 1),
+                        "frac_of_hbm_peak": round(row_op_bytes(w, n) / (row_us[n] * 1e-6) / 1e9
+                                                  / PEAK_HBM_GBS, 4)}
+                    for n in row_names},
     }
     if bal is not None:
         out["load_balancing"] = bal

@@ -47,3 +47,21 @@ def test_roofline_bound_follows_arithmetic_intensity():
     assert abs(big["achieved"] - flops / 2.0e-3 / 1e12) <= 0.01
     # HBM bytes from the counters are reported only for the source they were taken on
     assert (big["traffic"] is None) == (bench.traffic_of("gate_up_wgrad", WORKLOADS["fwdbwd"])["traffic"] is None)
+
+
+def test_row_op_bytes():
+    """Routing, permutation and combine are priced at their inputs read once and
+    outputs written once: at T = 8192 dots shapes the row copies dominate —
+    permute 2H(1+K)T, combine 2H(K+2)T, combine backward 2H(2K+1)T,
+    un-permute 2H(K+2)T + 4HT — plus their index and weight arrays."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from fine_grained_moe_amd.synthetic import WORKLOADS
+    w = WORKLOADS["fwdbwd"]
+    T, H, K = w.T, w.H, w.K
+    rows = {"permute": 2 * H * (1 + K) * T, "combine": 2 * H * (K + 2) * T,
+            "combine_bwd": 2 * H * (2 * K + 1) * T, "permute_bwd": 2 * H * (K + 2) * T + 4 * H * T,
+            "route": 2 * H * T, "route_bwd": 2 * H * K * T + 4 * H * T}
+    for n, b in rows.items():
+        got = bench.row_op_bytes(w, n)
+        assert b <= got <= b * 1.01 + 8e6, (n, got, b)
