@@ -88,6 +88,21 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
+def _expect(**items):
+    """name=(tensor, shape): every given tensor must have exactly that shape.
+    The library sees raw pointers only, so a buffer of the wrong size would be
+    read or written out of bounds; the binding refuses it instead."""
+    for name, (t, shape) in items.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _seg_shapes(G, M, offsets, counts, tile_expert):
+    """Segment tables of a grouped call (all None for a dense call)."""
+    A = int(_lib.moe_align())
+    _expect(offsets=(offsets, (G + 1,)), counts=(counts, (G,)), tile_expert=(tile_expert, (M // A,)))
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -141,6 +156,8 @@ def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=
     topk_s = torch.empty((T, K), dtype=F32, device=dev) if topk_s is None else topk_s
     if ws is None:
         ws = torch.empty(max(moe_route_workspace_bytes(T, H, E), 1), dtype=torch.uint8, device=dev)
+    _expect(w_router=(w_router, (H, E)), bias=(bias, (E,)), topk_idx=(topk_idx, (T, K)),
+            topk_w=(topk_w, (T, K)), topk_s=(topk_s, (T, K)), scores=(scores, (T, E)))
     _check(_lib.moe_route(T, H, E, K, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                           _ptr(bias, F32, "bias"), _ptr(topk_idx, I32, "topk_idx"),
                           _ptr(topk_w, F32, "topk_w"), _ptr(topk_s, F32, "topk_s"),
@@ -162,6 +179,9 @@ def moe_permute(topk_idx, x, E, m_cap=None, out=None, ws=None):
                    src_token=torch.empty(m_cap, dtype=I32, device=dev),
                    tile_expert=torch.empty(m_cap // A, dtype=I32, device=dev),
                    x_rows=torch.empty((m_cap, H), dtype=BF16, device=dev))
+    _expect(x=(x, (T, H)), counts=(out["counts"], (E,)), offsets=(out["offsets"], (E + 1,)),
+            row_of=(out["row_of"], (T, K)), src_token=(out["src_token"], (m_cap,)),
+            tile_expert=(out["tile_expert"], (m_cap // A,)), x_rows=(out["x_rows"], (m_cap, H)))
     nbytes = moe_permute_workspace_bytes(T, E, K)
     if ws is None:
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -187,6 +207,9 @@ def moe_grouped_swiglu_fwd(x_rows, w1, w2, offsets=None, counts=None, tile_exper
         act = None
     h = torch.empty((M, F), dtype=BF16, device=dev) if h is None else h
     y_rows = torch.empty((M, H), dtype=BF16, device=dev) if y_rows is None else y_rows
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w1=(w1, (G, 2 * F, H)), w2=(w2, (G, H, F)), act=(act, (M, 2 * F)), h=(h, (M, F)),
+            y_rows=(y_rows, (M, H)))
     _check(_lib.moe_grouped_swiglu_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
                                        _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
                                        _ptr(w1, BF16, "w1"), _ptr(w2, BF16, "w2"),
@@ -207,6 +230,8 @@ def moe_grouped_gate_up_fwd(x_rows, w1, offsets=None, counts=None, tile_expert=N
     elif act is False:
         act = None
     h = torch.empty((M, F), dtype=BF16, device=dev) if h is None else h
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w1=(w1, (G, 2 * F, H)), act=(act, (M, 2 * F)), h=(h, (M, F)))
     _check(_lib.moe_grouped_gate_up_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
                                         _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
                                         _ptr(w1, BF16, "w1"), _ptr(act, BF16, "act"),
@@ -219,6 +244,8 @@ def moe_grouped_down_fwd(h, w2, offsets=None, counts=None, tile_expert=None, y_r
     M, F = h.shape
     G, H, _ = w2.shape
     y_rows = torch.empty((M, H), dtype=BF16, device=h.device) if y_rows is None else y_rows
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w2=(w2, (G, H, F)), y_rows=(y_rows, (M, H)))
     _check(_lib.moe_grouped_down_fwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
                                      _ptr(tile_expert, I32), _ptr(h, BF16, "h"),
                                      _ptr(w2, BF16, "w2"), _ptr(y_rows, BF16, "y_rows"),
@@ -230,6 +257,7 @@ def moe_combine(y_rows, row_of, topk_w, y_shared=None, y=None):
     T, K = row_of.shape
     H = y_rows.shape[1]
     y = torch.empty((T, H), dtype=BF16, device=y_rows.device) if y is None else y
+    _expect(topk_w=(topk_w, (T, K)), y_shared=(y_shared, (T, H)), y=(y, (T, H)))
     _check(_lib.moe_combine(T, H, K, _ptr(y_rows, BF16, "y_rows"), _ptr(row_of, I32, "row_of"),
                             _ptr(topk_w, F32, "topk_w"), _ptr(y_shared, BF16, "y_shared"),
                             _ptr(y, BF16, "y"), _stream()))
@@ -243,6 +271,8 @@ def moe_combine_bwd(dy, y_rows, row_of, topk_w, dy_rows=None, dg=None):
     if dy_rows is None:
         dy_rows = torch.empty(y_rows.shape, dtype=BF16, device=dev)
     dg = torch.empty((T, K), dtype=F32, device=dev) if dg is None else dg
+    _expect(dy=(dy, (T, H)), y_rows=(y_rows, (y_rows.shape[0], H)), topk_w=(topk_w, (T, K)),
+            dy_rows=(dy_rows, tuple(y_rows.shape)), dg=(dg, (T, K)))
     _check(_lib.moe_combine_bwd(T, H, K, _ptr(dy, BF16, "dy"), _ptr(y_rows, BF16, "y_rows"),
                                 _ptr(row_of, I32, "row_of"), _ptr(topk_w, F32, "topk_w"),
                                 _ptr(dy_rows, BF16, "dy_rows"), _ptr(dg, F32, "dg"), _stream()))
@@ -260,6 +290,10 @@ def moe_grouped_swiglu_bwd(x_rows, w1, w2, act, h, dy_rows, offsets=None, counts
     dx_rows = torch.empty((M, H), dtype=BF16, device=dev) if dx_rows is None else dx_rows
     dw1 = torch.empty(w1.shape, dtype=BF16, device=dev) if dw1 is None else dw1
     dw2 = torch.empty(w2.shape, dtype=BF16, device=dev) if dw2 is None else dw2
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w1=(w1, (G, 2 * F, H)), w2=(w2, (G, H, F)), act=(act, (M, 2 * F)), h=(h, (M, F)),
+            dy_rows=(dy_rows, (M, H)), dact=(dact, (M, 2 * F)), dx_rows=(dx_rows, (M, H)),
+            dw1=(dw1, (G, 2 * F, H)), dw2=(dw2, (G, H, F)))
     _check(_lib.moe_grouped_swiglu_bwd(G, M, H, F, _ptr(offsets, I32), _ptr(counts, I32),
                                        _ptr(tile_expert, I32), _ptr(x_rows, BF16, "x_rows"),
                                        _ptr(w1, BF16, "w1"), _ptr(w2, BF16, "w2"),
@@ -280,6 +314,8 @@ def moe_grouped_down_dgrad(w2, act, dy_rows, offsets=None, counts=None, tile_exp
     M, H = dy_rows.shape
     G, _, F = w2.shape
     dact = torch.empty((M, 2 * F), dtype=BF16, device=dy_rows.device) if dact is None else dact
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w2=(w2, (G, H, F)), act=(act, (M, 2 * F)), dact=(dact, (M, 2 * F)))
     _check(_lib.moe_grouped_down_dgrad(G, M, H, F, *_seg(offsets, counts, tile_expert),
                                        _ptr(w2, BF16, "w2"), _ptr(act, BF16, "act"),
                                        _ptr(dy_rows, BF16, "dy_rows"), _ptr(dact, BF16, "dact"),
@@ -292,6 +328,8 @@ def moe_grouped_down_wgrad(dy_rows, h, G, offsets=None, counts=None, tile_expert
     M, H = dy_rows.shape
     F = h.shape[1]
     dw2 = torch.empty((G, H, F), dtype=BF16, device=h.device) if dw2 is None else dw2
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(h=(h, (M, F)), dw2=(dw2, (G, H, F)))
     _check(_lib.moe_grouped_down_wgrad(G, M, H, F, *_seg(offsets, counts, tile_expert),
                                        _ptr(dy_rows, BF16, "dy_rows"), _ptr(h, BF16, "h"),
                                        _ptr(dw2, BF16, "dw2"), _stream()))
@@ -303,6 +341,8 @@ def moe_grouped_gate_up_dgrad(w1, dact, offsets=None, counts=None, tile_expert=N
     M, twoF = dact.shape
     G, _, H = w1.shape
     dx_rows = torch.empty((M, H), dtype=BF16, device=dact.device) if dx_rows is None else dx_rows
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(w1=(w1, (G, twoF, H)), dx_rows=(dx_rows, (M, H)))
     _check(_lib.moe_grouped_gate_up_dgrad(G, M, H, twoF // 2, *_seg(offsets, counts, tile_expert),
                                           _ptr(w1, BF16, "w1"), _ptr(dact, BF16, "dact"),
                                           _ptr(dx_rows, BF16, "dx_rows"), _stream()))
@@ -315,6 +355,8 @@ def moe_grouped_gate_up_wgrad(dact, x_rows, G, offsets=None, counts=None, tile_e
     M, twoF = dact.shape
     H = x_rows.shape[1]
     dw1 = torch.empty((G, twoF, H), dtype=BF16, device=dact.device) if dw1 is None else dw1
+    _seg_shapes(G, M, offsets, counts, tile_expert)
+    _expect(x_rows=(x_rows, (M, H)), dw1=(dw1, (G, twoF, H)))
     _check(_lib.moe_grouped_gate_up_wgrad(G, M, H, twoF // 2, *_seg(offsets, counts, tile_expert),
                                           _ptr(dact, BF16, "dact"), _ptr(x_rows, BF16, "x_rows"),
                                           _ptr(dw1, BF16, "dw1"), _stream()))
@@ -331,6 +373,9 @@ def moe_route_bwd(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, count
     dx_router = torch.empty((T, H), dtype=F32, device=dev) if dx_router is None else dx_router
     nbytes = moe_route_bwd_workspace_bytes(T, H, E, K)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if ws is None else ws
+    _expect(x_rows=(x_rows, (x_rows.shape[0], H)), topk_s=(topk_s, (T, K)), dg=(dg, (T, K)),
+            row_of=(row_of, (T, K)), offsets=(offsets, (E + 1,)), counts=(counts, (E,)),
+            dw_router=(dw_router, (H, E)), dx_router=(dx_router, (T, H)))
     _check(_lib.moe_route_bwd(T, H, E, K, _ptr(x_rows, BF16, "x_rows"),
                               _ptr(w_router, F32, "w_router"), _ptr(topk_idx, I32, "topk_idx"),
                               _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
@@ -344,6 +389,7 @@ def moe_permute_bwd(dx_rows, row_of, dx_shared=None, dx_router=None, dx=None):
     T, K = row_of.shape
     H = dx_rows.shape[1]
     dx = torch.empty((T, H), dtype=BF16, device=dx_rows.device) if dx is None else dx
+    _expect(dx_shared=(dx_shared, (T, H)), dx_router=(dx_router, (T, H)), dx=(dx, (T, H)))
     _check(_lib.moe_permute_bwd(T, H, K, _ptr(dx_rows, BF16, "dx_rows"), _ptr(row_of, I32, "row_of"),
                                 _ptr(dx_shared, BF16, "dx_shared"), _ptr(dx_router, F32, "dx_router"),
                                 _ptr(dx, BF16, "dx"), _stream()))
@@ -353,6 +399,7 @@ def moe_permute_bwd(dx_rows, row_of, dx_shared=None, dx_router=None, dx=None):
 def moe_bias_update(counts, bias, gamma):
     """Updates bias (fp32 [E], in place) from the per-expert counts; returns bias."""
     E = bias.shape[0]
+    _expect(counts=(counts, (E,)), bias=(bias, (E,)))
     _check(_lib.moe_bias_update(E, _ptr(counts, I32, "counts"), _ptr(bias, F32, "bias"),
                                 float(gamma), _stream()))
     return bias
@@ -369,6 +416,7 @@ def moe_seq_balance_fwd(scores, topk_idx, seq_len, alpha, loss=None, seq_f=None,
     if ws is None:
         ws = torch.empty(max(moe_seq_balance_workspace_bytes(T, E, seq_len), 1), dtype=torch.uint8,
                          device=dev)
+    _expect(topk_idx=(topk_idx, (T, K)), loss=(loss, (1,)), seq_f=(seq_f, (max(B, 1), E)))
     _check(_lib.moe_seq_balance_fwd(T, E, K, seq_len, _ptr(scores, F32, "scores"),
                                     _ptr(topk_idx, I32, "topk_idx"), float(alpha),
                                     _ptr(loss, F32, "loss"), _ptr(seq_f, F32, "seq_f"), _ptr(ws),
@@ -380,6 +428,8 @@ def moe_seq_balance_bwd(scores, seq_f, K, seq_len, alpha, dloss=None, dlogit=Non
     """Returns dlogit [T,E] fp32 (dloss: fp32 [1] device tensor or None for 1)."""
     T, E = scores.shape
     dlogit = torch.empty((T, E), dtype=F32, device=scores.device) if dlogit is None else dlogit
+    B = T // seq_len if seq_len > 0 else 0
+    _expect(seq_f=(seq_f, (max(B, 1), E)), dloss=(dloss, (1,)), dlogit=(dlogit, (T, E)))
     _check(_lib.moe_seq_balance_bwd(T, E, K, seq_len, _ptr(scores, F32, "scores"),
                                     _ptr(seq_f, F32, "seq_f"), float(alpha),
                                     _ptr(dloss, F32, "dloss"), _ptr(dlogit, F32, "dlogit"),
@@ -392,6 +442,7 @@ def moe_route_dlogit(topk_idx, topk_s, dg, dlogit):
     dense fp32 dlogit [T,E], in place; returns dlogit."""
     T, K = topk_idx.shape
     E = dlogit.shape[1]
+    _expect(topk_s=(topk_s, (T, K)), dg=(dg, (T, K)), dlogit=(dlogit, (T, E)))
     _check(_lib.moe_route_dlogit(T, E, K, _ptr(topk_idx, I32, "topk_idx"),
                                  _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
                                  _ptr(dlogit, F32, "dlogit"), _stream()))
@@ -413,6 +464,8 @@ def moe_route_bwd_dense(x, w_router, dlogit, dw_router=None, dx_router=None, ws=
     if ws is None:
         ws = torch.empty(max(moe_route_bwd_dense_workspace_bytes(T, H, E), 1), dtype=torch.uint8,
                          device=x.device)
+    _expect(w_router=(w_router, (H, E)), dlogit=(dlogit, (T, E)), dw_router=(dw_router, (H, E)),
+            dx_router=(dx_router, (T, H)))
     _check(_lib.moe_route_bwd_dense(T, H, E, _ptr(x, BF16, "x"), _ptr(w_router, F32, "w_router"),
                                     _ptr(dlogit, F32, "dlogit"), _ptr(dw_router, F32, "dw_router"),
                                     _ptr(dx_router, F32, "dx_router"), 1 if accumulate else 0,

@@ -259,3 +259,30 @@ def test_segments_beyond_32_bit_offsets_rejected(lib):
                   ctypes.c_size_t, ctypes.c_void_p])
     assert d(6_000_000, 5120, 128, *[_p(None)] * 5, 1, _p(None), 0, _p(None)) == 2
     assert d(5_000_000, 5120, 128, *[_p(None)] * 5, 1, _p(None), 0, _p(None)) == 1   # null pointers
+
+
+def test_binding_rejects_wrong_shapes():
+    """The library sees raw pointers only; the binding refuses a buffer whose
+    shape differs from what the call reads or writes (checked before any
+    device pointer is taken, so this runs on the CPU)."""
+    import pytest
+    torch = pytest.importorskip("torch")
+    from fine_grained_moe_amd import moe as M
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    T, H, K, E = 4, 64, 2, 8
+    y_rows = torch.empty((1024, H), dtype=bf)
+    row_of = torch.empty((T, K), dtype=i32)
+    with pytest.raises(ValueError, match="topk_w"):
+        M.moe_combine(y_rows, row_of, torch.empty((T, K + 1), dtype=f32))
+    with pytest.raises(ValueError, match="y must have shape"):
+        M.moe_combine(y_rows, row_of, torch.empty((T, K), dtype=f32), y=torch.empty((T - 1, H), dtype=bf))
+    with pytest.raises(ValueError, match="dw1"):
+        M.moe_grouped_gate_up_wgrad(torch.empty((256, 64), dtype=bf), torch.empty((256, H), dtype=bf), 2,
+                                    dw1=torch.empty((1, 64, H), dtype=bf))
+    with pytest.raises(ValueError, match="tile_expert"):
+        M.moe_grouped_down_fwd(torch.empty((256, 32), dtype=bf), torch.empty((2, H, 32), dtype=bf),
+                               torch.empty(3, dtype=i32), torch.empty(2, dtype=i32),
+                               torch.empty(3, dtype=i32))
+    with pytest.raises(ValueError, match="dlogit"):
+        M.moe_route_dlogit(row_of, torch.empty((T, K), dtype=f32), torch.empty((T, K), dtype=f32),
+                           torch.empty((T - 1, E), dtype=f32))
