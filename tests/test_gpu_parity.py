@@ -477,3 +477,25 @@ def test_ep_shard_sampled(M):
             P.assert_close(f"shard dW1[{e},{f}] gate", P.to_np(dw1[e, f]), dw1u[0])
             P.assert_close(f"shard dW1[{e},{f}] up", P.to_np(dw1[e, F + f]), dw1u[1])
             P.assert_close(f"shard dW2[{e}][:,{f}]", P.to_np(dw2[e][:, f]), dw2u[:, 0])
+
+
+def test_inference_forward_without_saved_activations(M):
+    """save_for_backward=False skips the gate/up activations (the epilogue
+    writes h only); h, the expert rows and y are bit-identical to the training
+    forward, routed and shared."""
+    w = MID["T1000_H512_E16_K4_F352"]
+    inp = generate_numpy(w, with_dy=False)
+    g = {k: torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(DEV) for k, v in inp.items()}
+    for k in ("x", "w1", "w2", "w1_sh", "w2_sh"):
+        g[k] = g[k].to(torch.bfloat16)
+    w1f, w2f = M.fuse_shared(g["w1_sh"], g["w2_sh"])
+    args = (g["x"], g["w_router"], g["bias"], g["w1"], g["w2"], w1f, w2f, w.K)
+    y_t, ctx_t = M.layer_forward(*args, save_for_backward=True)
+    y_i, ctx_i = M.layer_forward(*args, save_for_backward=False)
+    torch.cuda.synchronize()
+    assert ctx_i["act"] is None and ctx_i["act_sh"] is None
+    assert torch.equal(y_i, y_t)
+    valid = ctx_t["perm"]["src_token"] >= 0
+    assert torch.equal(ctx_i["h"][valid], ctx_t["h"][valid])
+    assert torch.equal(ctx_i["y_rows"][valid], ctx_t["y_rows"][valid])
+    assert torch.equal(ctx_i["h_sh"], ctx_t["h_sh"])
