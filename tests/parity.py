@@ -108,6 +108,10 @@ def check_route(gpu_idx, gpu_w, gpu_s, ref, label=""):
     if same.any():
         assert_close(f"{label} topk_w", gpu_w[same], ref["topk_w"][same])
         assert_close(f"{label} topk_s", gpu_s[same], ref["topk_s"][same], tol=1e-5, norm_tol=1e-5)
+    print(f"  {label} routing: {int((~set_same).sum())} tokens select another set (all near-ties: "
+          f"{int(ref['near_tie'].sum())} in the batch), {int((set_same & ~same).sum())} list the same "
+          f"set in another order (all within order-tie keys: {int(ref['order_tie'].sum())} in the "
+          f"batch)", flush=True)
     return int((~same).sum()), int(ref["near_tie"].sum())
 
 
