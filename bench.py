@@ -5,7 +5,8 @@ grouped SwiGLU GEMMs, combine, and their backward) over T=8192 tokens at
 dots.llm1 shapes (H=5120, 128 routed experts of width 1408, top-6, 2 shared
 experts), synthetic seeded inputs resident in HBM.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-balance]
+    python bench.py [--steps K] [--warmup W] [--workload fwdbwd|prefill|decode|skew|ep_shard]
+                    [--no-cpu-baseline] [--no-balance] [--no-graph] [--copy-calibration]
 """
 from __future__ import annotations
 
