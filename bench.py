@@ -209,9 +209,9 @@ class Layer:
             b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"]))
         if not balance:
             self._gemm("route_bwd", ev, lambda: M.moe_route_bwd(
-                p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
-                p["offsets"], p["counts"], dw_router=b["dw_router"], dx_router=b["dx_router"],
-                ws=b["rb_ws"]))
+                g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
+                p["offsets"], p["counts"], p["src_token"], dw_router=b["dw_router"],
+                dx_router=b["dx_router"], ws=b["rb_ws"]))
         else:
             # the balance loss's dense logit gradient, the combine path's added
             # into it, and one dense router backward for both
@@ -280,8 +280,8 @@ class Layer:
             M.moe_grouped_down_wgrad(g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"])
             M.moe_grouped_gate_up_wgrad(b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"])
         M.moe_grouped_gate_up_dgrad(g["w1"], b["dact"], *seg, dx_rows=b["dx_rows"])
-        M.moe_route_bwd(p["x_rows"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
-                        p["offsets"], p["counts"], dw_router=b["dw_router"],
+        M.moe_route_bwd(g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
+                        p["offsets"], p["counts"], p["src_token"], dw_router=b["dw_router"],
                         dx_router=b["dx_router"], ws=b["rb_ws"])
         main.wait_stream(side)
         M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
@@ -307,8 +307,9 @@ def row_op_bytes(w, name):
         return tk * row + (T * row if w.S else 0) + 8 * tk + T * row
     if name == "combine_bwd":  # dy, y_rows, row_of, topk_w in; dy_rows, dg out
         return T * row + tk * row + 8 * tk + tk * row + 4 * tk
-    if name == "route_bwd":    # x_rows, W_r, topk_idx/s, dg, row_of in; dW_r, dx_router out
-        return tk * row + 4 * H * E + 16 * tk + 4 * H * E + 4 * T * H
+    if name == "route_bwd":    # x, W_r, topk_idx/s, dg, row_of, src_token in; dW_r, dx_router out
+        m_cap = ((tk + E * 127 + 127) // 128) * 128
+        return T * row + 4 * H * E + 16 * tk + 4 * m_cap + 4 * H * E + 4 * T * H
     if name == "permute_bwd":  # dx_rows, dx_shared, dx_router, row_of in; dx out
         return tk * row + (T * row if w.S else 0) + 4 * T * H + 4 * tk + T * row
     raise KeyError(name)

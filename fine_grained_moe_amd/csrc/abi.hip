@@ -338,24 +338,24 @@ moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int
                     __func__);
 }
 
-moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x_rows,
+moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
                            const float* w_router, const int32_t* topk_idx, const float* topk_s,
                            const float* dg, const int32_t* row_of, const int32_t* offsets,
-                           const int32_t* counts, float* dw_router, float* dx_router, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           const int32_t* counts, const int32_t* src_token, float* dw_router,
+                           float* dx_router, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_dims(__func__, T, H, E, K);
   if (st) return st;
   REQUIRE(w_router && offsets && counts && dw_router, MOE_ERR_INVALID_ARGUMENT, "null pointer");
-  REQUIRE(T == 0 || (x_rows && topk_idx && topk_s && dg && row_of && dx_router),
+  REQUIRE(T == 0 || (x && topk_idx && topk_s && dg && row_of && src_token && dx_router),
           MOE_ERR_INVALID_ARGUMENT, "null pointer");
   REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_workspace_bytes(T, H, E, K),
           MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
-  REQUIRE_ALIGNED(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, dw_router,
+  REQUIRE_ALIGNED(x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token, dw_router,
                   dx_router);
   REQUIRE_WS_ALIGNED(ws);
   // T == 0 still writes the (zero) router weight gradient
-  return hip_status(moe::launch_route_bwd(T, H, E, K, x_rows, w_router, topk_idx, topk_s, dg,
-                                          row_of, offsets, counts, dw_router, dx_router, ws,
+  return hip_status(moe::launch_route_bwd(T, H, E, K, x, w_router, topk_idx, topk_s, dg, row_of,
+                                          offsets, counts, src_token, dw_router, dx_router, ws,
                                           (hipStream_t)stream),
                     __func__);
 }

@@ -60,11 +60,11 @@ hipError_t launch_unpermute_add(int T, int H, int K, const uint16_t* dx_rows,
                                 const int32_t* row_of, const uint16_t* dx_shared,
                                 const float* dx_router, uint16_t* dx, hipStream_t s);
 size_t route_bwd_workspace_bytes(int64_t m_cap, int H, int E);
-hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x_rows,
+hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x,
                             const float* w_router, const int32_t* topk_idx, const float* topk_s,
                             const float* dg, const int32_t* row_of, const int32_t* offsets,
-                            const int32_t* counts, float* dw_router, float* dx_router, void* ws,
-                            hipStream_t s);
+                            const int32_t* counts, const int32_t* src_token, float* dw_router,
+                            float* dx_router, void* ws, hipStream_t s);
 
 
 hipError_t launch_bias_update(int E, const int32_t* counts, float* bias, float gamma,

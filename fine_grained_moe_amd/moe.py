@@ -48,7 +48,7 @@ _SIGS = {
     "moe_grouped_gate_up_dgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_gate_up_wgrad": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_route_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
-                             _sz, _p]),
+                             _p, _sz, _p]),
     "moe_permute_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_bias_update": (_i32, [_i32, _p, _p, ctypes.c_float, _p]),
     "moe_seq_balance_fwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p, _sz,
@@ -363,9 +363,11 @@ def moe_grouped_gate_up_wgrad(dact, x_rows, G, offsets=None, counts=None, tile_e
     return dw1
 
 
-def moe_route_bwd(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, counts,
+def moe_route_bwd(x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token,
                   dw_router=None, dx_router=None, ws=None):
-    """Returns (dw_router [H,E] fp32, dx_router [T,H] fp32)."""
+    """Router gradients of the combine path (x [T,H] bf16 and moe_permute's
+    row_of, offsets, counts and src_token).  Returns (dw_router [H,E] fp32,
+    dx_router [T,H] fp32)."""
     T, K = topk_idx.shape
     H, E = w_router.shape
     dev = w_router.device
@@ -373,15 +375,19 @@ def moe_route_bwd(x_rows, w_router, topk_idx, topk_s, dg, row_of, offsets, count
     dx_router = torch.empty((T, H), dtype=F32, device=dev) if dx_router is None else dx_router
     nbytes = moe_route_bwd_workspace_bytes(T, H, E, K)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if ws is None else ws
-    _expect(x_rows=(x_rows, (x_rows.shape[0], H)), topk_s=(topk_s, (T, K)), dg=(dg, (T, K)),
-            row_of=(row_of, (T, K)), offsets=(offsets, (E + 1,)), counts=(counts, (E,)),
+    _expect(x=(x, (T, H)), topk_s=(topk_s, (T, K)), dg=(dg, (T, K)), row_of=(row_of, (T, K)),
+            offsets=(offsets, (E + 1,)), counts=(counts, (E,)),
+            src_token=(src_token, (src_token.shape[0],) if src_token is not None else ()),
             dw_router=(dw_router, (H, E)), dx_router=(dx_router, (T, H)))
-    _check(_lib.moe_route_bwd(T, H, E, K, _ptr(x_rows, BF16, "x_rows"),
+    if src_token is not None and src_token.shape[0] < moe_capacity_rows(T, E, K):
+        raise ValueError("src_token must hold at least moe_capacity_rows(T, E, K) entries")
+    _check(_lib.moe_route_bwd(T, H, E, K, _ptr(x, BF16, "x"),
                               _ptr(w_router, F32, "w_router"), _ptr(topk_idx, I32, "topk_idx"),
                               _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
                               _ptr(row_of, I32, "row_of"), _ptr(offsets, I32, "offsets"),
-                              _ptr(counts, I32, "counts"), _ptr(dw_router, F32, "dw_router"),
-                              _ptr(dx_router, F32, "dx_router"), _ptr(ws), ws.numel(), _stream()))
+                              _ptr(counts, I32, "counts"), _ptr(src_token, I32, "src_token"),
+                              _ptr(dw_router, F32, "dw_router"), _ptr(dx_router, F32, "dx_router"),
+                              _ptr(ws), ws.numel(), _stream()))
     return dw_router, dx_router
 
 
@@ -528,9 +534,9 @@ def layer_backward(dy, ctx, dloss=None):
                                                           ctx["act_sh"], ctx["h_sh"], dy)
     dlogit_bal = dlogit = None
     if ctx.get("balance") is None:
-        dw_router, dx_router = moe_route_bwd(p["x_rows"], ctx["w_router"], ctx["topk_idx"],
+        dw_router, dx_router = moe_route_bwd(ctx["x"], ctx["w_router"], ctx["topk_idx"],
                                              ctx["topk_s"], dg, p["row_of"], p["offsets"],
-                                             p["counts"])
+                                             p["counts"], p["src_token"])
     else:
         # the balance loss's logit gradient is dense; the combine path's is
         # added into (a copy of) it, and one dense router backward gives the

@@ -280,16 +280,18 @@ moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int
  *   dlogit[t,k]= ds[t,k] * s * (1 - s),   s = topk_s[t,k]
  *   dw_router[h,e] = sum over tokens t that selected e of x[t,h] * dlogit   (fp32 [H,E])
  *   dx_router[t,h] = sum_k dlogit[t,k] * w_router[h, topk_idx[t,k]]        (fp32 [T,H])
- * The weight gradient is summed over expert segments, so it takes the
- * permutation: x_rows, row_of, offsets, counts from moe_permute.
+ * The weight gradient is summed over expert segments in fixed order, so it
+ * takes the permutation from moe_permute (row_of, offsets, counts, and
+ * src_token, whose entries below offsets[E] name the token of every row) and
+ * gathers the token rows from x [T,H] bf16.
  * ws: device workspace of at least moe_route_bwd_workspace_bytes(T,H,E,K).
  */
 moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K,
-                           const uint16_t* x_rows, const float* w_router,
+                           const uint16_t* x, const float* w_router,
                            const int32_t* topk_idx, const float* topk_s, const float* dg,
                            const int32_t* row_of, const int32_t* offsets,
-                           const int32_t* counts, float* dw_router, float* dx_router,
-                           void* ws, size_t ws_bytes, void* stream);
+                           const int32_t* counts, const int32_t* src_token, float* dw_router,
+                           float* dx_router, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_permute_bwd - un-permute and add every path of the input gradient:

@@ -144,9 +144,11 @@ def test_row_kernels_reject(lib):
 
 def test_route_bwd_rejects(lib):
     f = lib.moe_route_bwd
-    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]
-    assert f(16, 64, 8, 2, *[_p(FAKE)] * 11, 16, _p(None)) == 3
-    assert f(16, 64, 8, 2, _p(None), *[_p(FAKE)] * 10, 1 << 30, _p(None)) == 1
+    # x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token, dw_router, dx_router, ws
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 12, 16, _p(None)) == 3
+    assert f(16, 64, 8, 2, _p(None), *[_p(FAKE)] * 11, 1 << 30, _p(None)) == 1
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 8, _p(None), *[_p(FAKE)] * 3, 1 << 30, _p(None)) == 1  # src_token
 
 
 def test_backward_steps_reject(lib):

@@ -53,7 +53,8 @@ def test_row_op_bytes():
     """Routing, permutation and combine are priced at their inputs read once and
     outputs written once: at T = 8192 dots shapes the row copies dominate —
     permute 2H(1+K)T, combine 2H(K+2)T, combine backward 2H(2K+1)T,
-    un-permute 2H(K+2)T + 4HT — plus their index and weight arrays."""
+    un-permute 2H(K+2)T + 4HT, router backward 2HT + 4HT (x gathered, dx_router
+    written) — plus their index and weight arrays."""
     sys.path.insert(0, ROOT)
     import bench
     from fine_grained_moe_amd.synthetic import WORKLOADS
@@ -61,7 +62,7 @@ def test_row_op_bytes():
     T, H, K = w.T, w.H, w.K
     rows = {"permute": 2 * H * (1 + K) * T, "combine": 2 * H * (K + 2) * T,
             "combine_bwd": 2 * H * (2 * K + 1) * T, "permute_bwd": 2 * H * (K + 2) * T + 4 * H * T,
-            "route": 2 * H * T, "route_bwd": 2 * H * K * T + 4 * H * T}
+            "route": 2 * H * T, "route_bwd": 2 * H * T + 4 * H * T}
     for n, b in rows.items():
         got = bench.row_op_bytes(w, n)
         assert b <= got <= b * 1.01 + 8e6, (n, got, b)

@@ -279,7 +279,8 @@ def test_empty_batch(M):
     _, _, dw1, dw2 = M.moe_grouped_swiglu_bwd(p["x_rows"], w1, w2, act, h, dy_rows, p["offsets"],
                                               p["counts"], p["tile_expert"])
     dg = torch.zeros((0, K), device=DEV)
-    dwr, dxr = M.moe_route_bwd(p["x_rows"], wr, idx, ts, dg, p["row_of"], p["offsets"], p["counts"])
+    dwr, dxr = M.moe_route_bwd(x, wr, idx, ts, dg, p["row_of"], p["offsets"], p["counts"],
+                               p["src_token"])
     torch.cuda.synchronize()
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
 

@@ -238,8 +238,8 @@ def test_one_dense_router_backward_equals_sparse_plus_dense(M):
     gen.manual_seed(71)
     dg = torch.randn((w.T, w.K), generator=gen, device=DEV)
     dl_bal = torch.randn((w.T, w.E), generator=gen, device=DEV) * 1e-4
-    dw_a, dx_a = M.moe_route_bwd(p["x_rows"], g["w_router"], idx, ts, dg, p["row_of"],
-                                 p["offsets"], p["counts"])
+    dw_a, dx_a = M.moe_route_bwd(g["x"], g["w_router"], idx, ts, dg, p["row_of"],
+                                 p["offsets"], p["counts"], p["src_token"])
     M.moe_route_bwd_dense(g["x"], g["w_router"], dl_bal, dw_a, dx_a)
     dl = M.moe_route_dlogit(idx, ts, dg, dl_bal.clone())
     dw_b, dx_b = M.moe_route_bwd_dense(g["x"], g["w_router"], dl, accumulate=False)
