@@ -38,12 +38,12 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "dd60b090cf2d5b9a543a4abe10275ceb9112f7fc2064409d1c3162685572bb78"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3092961.9, 405504.0), "down_fwd": (1085185.9, 491548.5),
-    "shared_gate_up_fwd": (348240.3, 135196.2), "shared_down_fwd": (180294.2, 81968.0),
-    "down_dgrad": (1924041.4, 270336.2), "gate_up_dgrad": (2562536.4, 491527.2),
-    "down_wgrad": (322354.3, 1802285.4), "gate_up_wgrad": (847620.0, 3605167.6),
-    "shared_down_dgrad": (352472.6, 90130.5), "shared_gate_up_dgrad": (360522.3, 81970.9),
-    "shared_down_wgrad": (217162.8, 28169.2), "shared_gate_up_wgrad": (434252.0, 56354.3),
+    "gate_up_fwd": (3074073.3, 405504.0), "down_fwd": (1100880.6, 491522.5),
+    "shared_gate_up_fwd": (348240.3, 135193.2), "shared_down_fwd": (180294.3, 81948.4),
+    "down_dgrad": (1889594.3, 270336.0), "gate_up_dgrad": (2572861.2, 491520.8),
+    "down_wgrad": (321295.5, 1802300.7), "gate_up_wgrad": (847130.9, 3605096.5),
+    "shared_down_dgrad": (352390.9, 90132.2), "shared_gate_up_dgrad": (360522.4, 81922.4),
+    "shared_down_wgrad": (217162.8, 28160.8), "shared_gate_up_wgrad": (434252.0, 56321.0),
 }
 
 
