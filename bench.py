@@ -381,7 +381,14 @@ def cpu_baseline(w, g, n_tokens, gpu=None):
     dt = time.perf_counter() - t0
     flops = useful_flops(w.with_(T=n_tokens), backward)
     cores = len(os.sched_getaffinity(0))
-    res = dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    res = dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, cpu_model=cpu_model,
+               kind="oracle",
                sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
                        f"first {n_tokens} of the {w.T} tokens at the same shapes, one run, "
                        f"{dt:.1f} s; BLAS threads {threads}"),
