@@ -250,15 +250,31 @@ __global__ void __launch_bounds__(SEL_NT) select_kernel(int T, int E, int K, int
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * SEL_TPB + (threadIdx.x >> 6);
   if (t >= T) return;
+  // slice logits: eight slices' loads in flight at a time (small batches run
+  // with up to 64 slices), added in slice order
+  float z[2] = {0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        v[u][q] = (s0 + u < S && lane + 64 * q < E)
+                      ? part[((int64_t)(s0 + u) * T + t) * EMAX + lane + 64 * q]
+                      : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (s0 + u < S) z[q] += v[u][q];
+  }
   float sc[2];
   uint64_t key[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = lane + 64 * q;
     if (e < E) {
-      float z = 0.f;
-      for (int sl = 0; sl < S; ++sl) z += part[((int64_t)sl * T + t) * EMAX + e];
-      sc[q] = 1.0f / (1.0f + expf(-z));
+      sc[q] = 1.0f / (1.0f + expf(-z[q]));
       if (scores) scores[(int64_t)t * E + e] = sc[q];
       const float v = sc[q] + bias[e];
       key[q] = ((uint64_t)order_code(v) << 32) | (uint32_t)(0xFFFFu - e);
