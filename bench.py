@@ -38,12 +38,12 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "dd60b090cf2d5b9a543a4abe10275ceb9112f7fc2064409d1c3162685572bb78"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3074073.3, 405504.0), "down_fwd": (1100880.6, 491522.5),
-    "shared_gate_up_fwd": (348240.3, 135193.2), "shared_down_fwd": (180294.3, 81948.4),
-    "down_dgrad": (1889594.3, 270336.0), "gate_up_dgrad": (2572861.2, 491520.8),
-    "down_wgrad": (321295.5, 1802300.7), "gate_up_wgrad": (847130.9, 3605096.5),
-    "shared_down_dgrad": (352390.9, 90132.2), "shared_gate_up_dgrad": (360522.4, 81922.4),
-    "shared_down_wgrad": (217162.8, 28160.8), "shared_gate_up_wgrad": (434252.0, 56321.0),
+    "gate_up_fwd": (3082555.8, 405504.0), "down_fwd": (1112652.5, 491525.2),
+    "shared_gate_up_fwd": (348240.3, 135188.8), "shared_down_fwd": (180294.3, 81958.6),
+    "down_dgrad": (1903983.2, 270336.8), "gate_up_dgrad": (2556794.1, 491520.4),
+    "down_wgrad": (321956.6, 1802274.4), "gate_up_wgrad": (847341.4, 3604965.0),
+    "shared_down_dgrad": (352378.3, 90126.7), "shared_gate_up_dgrad": (360522.4, 81920.9),
+    "shared_down_wgrad": (217162.8, 28161.4), "shared_gate_up_wgrad": (434252.0, 56320.6),
 }
 
 
