@@ -432,6 +432,26 @@ def test_fwdbwd_sampled(M):
     sampled_checks(M, WORKLOADS["fwdbwd"], backward=True)
 
 
+# The largest token count a training step accepts at dots shapes: the weight
+# gradients address a segment of rows through 32-bit byte offsets, so the
+# permuted capacity times a 10 KB row (H = 5120 bf16) must stay below 4 GiB.
+# T is not a multiple of 32 either, so the last row tiles are ragged.
+MAX_T = 67178
+
+
+@pytest.mark.timeout(900)
+def test_max_tokens_sampled(M):
+    """Forward and backward at the largest accepted T: byte offsets of the
+    permuted rows run past 2 GiB and up to 4 GiB, which every row kernel and
+    GEMM tile must address in 64 bits or as unsigned 32-bit buffer offsets."""
+    row_bytes = 2 * 5120
+    m_cap = M.moe_capacity_rows(MAX_T, 128, 6)
+    assert m_cap * row_bytes < 1 << 32 <= M.moe_capacity_rows(MAX_T + 1, 128, 6) * row_bytes
+    assert m_cap * row_bytes > 1 << 31
+    w = Workload("max_tokens", T=MAX_T, H=5120, E=128, K=6, S=2, F=1408, seed=6, backward=True)
+    sampled_checks(M, w, backward=True, n_tokens=16)
+
+
 @pytest.mark.timeout(600)
 def test_ep_shard_sampled(M):
     """The six routed grouped products at one GPU's share of an 8-way
