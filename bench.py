@@ -60,12 +60,12 @@ def traffic_of(name, w):
             "traffic_write_gb": round(wk * COUNTER_FACTORS["WRITE_SIZE"] * 1024 / 1e9, 3)}
 
 
-def roofline_of(name, w, launch_ms, traffic=True):
+def roofline_of(name, w, launch_ms, traffic=True, live=None):
     """Roofline entry of one grouped-GEMM launch: MFMA-bound (useful TFLOP/s
     against the bf16 peak) when its arithmetic intensity (useful flops per
     algorithmic byte) is at or above the ridge, else HBM-bound (algorithmic
-    GB/s against 8 TB/s)."""
-    flops, nbytes = gemm_launch_flops(w, name), gemm_launch_bytes(w, name)
+    GB/s against 8 TB/s).  `live`: routed experts that own rows."""
+    flops, nbytes = gemm_launch_flops(w, name), gemm_launch_bytes(w, name, live)
     sec = launch_ms * 1e-3
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     tf, gbs = flops / sec / 1e12, nbytes / sec / 1e9
@@ -325,12 +325,17 @@ def gemm_launch_flops(w, name):
     return 2.0 * rows * w.H * F * mult
 
 
-def gemm_launch_bytes(w, name):
+def gemm_launch_bytes(w, name, live=None):
     """Algorithmic HBM bytes of one launch: every operand read once and every
-    result written once, bf16, padding rows excluded."""
+    result written once, bf16, padding rows excluded.  `live` is the number of
+    routed experts that own rows (default all E): the forward and data-gradient
+    products read only their weights, while the weight gradients write all E
+    (zeros for an expert without rows)."""
     shared = name.startswith("shared_")
     rows = w.T if shared else w.T * w.K
     G = 1 if shared else w.E
+    if not shared and live is not None and not name.endswith("wgrad"):
+        G = live
     F = w.S * w.F if shared else w.F
     H = w.H
     wt = 2 * G * 2 * F * H if "gate_up" in name else 2 * G * H * F      # one weight tensor
@@ -667,9 +672,10 @@ def main():
     # the dominant kernel: the grouped-GEMM launch with the longest average time
     dom = max(names, key=lambda n: launch_ms[n])
     counts = layer.b["perm"]["counts"].cpu().numpy()
+    live = int((counts > 0).sum())
     launches = {n: {"ms": round(launch_ms[n], 4),
                     "tflops": round(gemm_launch_flops(w, n) / (launch_ms[n] * 1e-3) / 1e12, 1),
-                    "algorithmic_gb": round(gemm_launch_bytes(w, n) / 1e9, 3)} for n in names}
+                    "algorithmic_gb": round(gemm_launch_bytes(w, n, live) / 1e9, 3)} for n in names}
 
     out = {
         "metric": "MoE layer useful TFLOP/s at T=8192 (fwd, fwd+bwd); % of bf16 MFMA peak",
@@ -698,8 +704,8 @@ def main():
         "gemm_ms": round(gemm_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "graph_two_streams_ms_per_step": None if graph2_ms is None else round(graph2_ms, 4),
-        "routed_nonempty_experts": int((counts > 0).sum()),
-        "roofline": roofline_of(dom, w, launch_ms[dom]),
+        "routed_nonempty_experts": live,
+        "roofline": roofline_of(dom, w, launch_ms[dom], live=live),
         "gemm_launches": launches,
         # routing, permutation and combine: algorithmic bytes (every input read
         # once, every output written once) over the call's time, against 8 TB/s

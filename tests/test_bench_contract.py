@@ -28,6 +28,12 @@ def test_gemm_flop_and_byte_accounting():
     rows = w.T * w.K
     exp = 2 * (rows * w.H + w.E * 2 * w.F * w.H + rows * 3 * w.F)
     assert bench.gemm_launch_bytes(w, "gate_up_fwd") == exp
+    # experts without rows: their weights are not read, but their (zero)
+    # weight gradients are still written
+    wt1 = 2 * 2 * w.F * w.H
+    assert bench.gemm_launch_bytes(w, "gate_up_fwd", live=20) == exp - (w.E - 20) * wt1
+    assert bench.gemm_launch_bytes(w, "gate_up_wgrad", live=20) == bench.gemm_launch_bytes(w, "gate_up_wgrad")
+    assert bench.gemm_launch_bytes(w, "shared_gate_up_fwd", live=20) == bench.gemm_launch_bytes(w, "shared_gate_up_fwd")
 
 
 def test_roofline_bound_follows_arithmetic_intensity():
