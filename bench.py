@@ -141,6 +141,9 @@ class Layer:
             seq_ws=e(max(M.moe_seq_balance_workspace_bytes(T, E, SEQ_LEN), 1), dt=torch.uint8),
             dloss=torch.ones(1, dtype=f32, device=dev), dlogit_bal=e(T, E, dt=f32),
             dense_ws=e(max(M.moe_route_bwd_dense_workspace_bytes(T, H, E), 1), dt=torch.uint8),
+            # the shared experts' forward at small T splits its contraction
+            # over workgroups into fp32 partial products
+            split_ws=e(max(M.moe_dense_fwd_split_workspace_bytes(T, H, SF), 1), dt=torch.uint8),
             bias_train=g["bias"].clone())
         self.ev = None
 
@@ -175,10 +178,10 @@ class Layer:
             p["x_rows"], g["w1"], *seg, act=b["act"], h=b["h"]))
         self._gemm("down_fwd", ev, lambda: M.moe_grouped_down_fwd(
             b["h"], g["w2"], *seg, y_rows=b["y_rows"]))
-        self._gemm("shared_gate_up_fwd", ev, lambda: M.moe_grouped_gate_up_fwd(
-            g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"]))
-        self._gemm("shared_down_fwd", ev, lambda: M.moe_grouped_down_fwd(
-            b["h_sh"], self.w2f, y_rows=b["y_sh"]))
+        self._gemm("shared_gate_up_fwd", ev, lambda: M.moe_dense_gate_up_fwd_split(
+            g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"], ws=b["split_ws"]))
+        self._gemm("shared_down_fwd", ev, lambda: M.moe_dense_down_fwd_split(
+            b["h_sh"], self.w2f, y=b["y_sh"], ws=b["split_ws"]))
         self._gemm("combine", ev, lambda: M.moe_combine(
             b["y_rows"], p["row_of"], b["topk_w"], b["y_sh"], y=b["y"]))
 
@@ -252,8 +255,9 @@ class Layer:
 
         side.wait_event(mark(main))
         with torch.cuda.stream(side):
-            M.moe_grouped_gate_up_fwd(g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"])
-            M.moe_grouped_down_fwd(b["h_sh"], self.w2f, y_rows=b["y_sh"])
+            M.moe_dense_gate_up_fwd_split(g["x"], self.w1f, act=b["act_sh"], h=b["h_sh"],
+                                          ws=b["split_ws"])
+            M.moe_dense_down_fwd_split(b["h_sh"], self.w2f, y=b["y_sh"], ws=b["split_ws"])
             shared_fwd = mark(side)
             if backward:
                 M.moe_grouped_down_dgrad(self.w2f, b["act_sh"], g["dy"], dact=b["dact_sh"])

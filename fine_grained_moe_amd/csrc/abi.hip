@@ -220,6 +220,42 @@ moe_status_t moe_grouped_down_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t 
                     __func__);
 }
 
+size_t moe_dense_fwd_split_workspace_bytes(int64_t m_rows, int32_t H, int32_t F) {
+  if (m_rows <= 0 || H <= 0 || F <= 0) return 0;
+  return moe::dense_fwd_split_workspace_bytes(m_rows, H, F);
+}
+
+moe_status_t moe_dense_gate_up_fwd_split(int64_t m_rows, int32_t H, int32_t F, const uint16_t* x,
+                                         const uint16_t* w1, uint16_t* act, uint16_t* h, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  moe_status_t st = check_grouped(__func__, 1, m_rows, H, F, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(x && w1 && h, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(x, w1, act, h);
+  REQUIRE_WS_ALIGNED(ws);
+  const size_t need = moe::dense_fwd_split_workspace_bytes(m_rows, H, F);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return hip_status(
+      moe::launch_dense_gate_up_split(m_rows, H, F, x, w1, act, h, ws, (hipStream_t)stream),
+      __func__);
+}
+
+moe_status_t moe_dense_down_fwd_split(int64_t m_rows, int32_t H, int32_t F, const uint16_t* h,
+                                      const uint16_t* w2, uint16_t* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  moe_status_t st = check_grouped(__func__, 1, m_rows, H, F, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (m_rows == 0) return MOE_OK;
+  REQUIRE(h && w2 && y, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(h, w2, y);
+  REQUIRE_WS_ALIGNED(ws);
+  const size_t need = moe::dense_fwd_split_workspace_bytes(m_rows, H, F);
+  REQUIRE(ws_bytes >= need && (need == 0 || ws), MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  return hip_status(moe::launch_dense_down_split(m_rows, H, F, h, w2, y, ws, (hipStream_t)stream),
+                    __func__);
+}
+
 moe_status_t moe_combine(int32_t T, int32_t H, int32_t K, const uint16_t* y_rows,
                          const int32_t* row_of, const float* topk_w, const uint16_t* y_shared,
                          uint16_t* y, void* stream) {

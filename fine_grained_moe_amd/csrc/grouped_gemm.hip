@@ -120,6 +120,8 @@ struct Args {
   int n_mtiles, n_ntiles, G;
   float* Cf;             // F32: fp32 output (row-major, ldc)
   int acc_out;           // F32: add to Cf instead of writing it
+  int ksplit;            // F32, dense MGROUP: slices of the k range (0 or 1: none)
+  int64_t split_stride;  // F32 with ksplit > 1: elements between slices' outputs
 };
 
 // MN-contig tile of BK k-rows x C columns.  A 1 KB region holds KPR k-rows.
@@ -218,9 +220,15 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   // (not the grid) over the XCDs keeps every XCD busy; the surplus ids exit.
   int n_mt = a.n_mtiles;
   if (MODE == MGROUP && a.tile_expert != nullptr) n_mt = a.offsets[a.G] / BM;
-  const int ntiles_live = (MODE == MGROUP) ? n_mt * a.n_ntiles : (int)gridDim.x;
+  // k split (dense fp32-output products only): the grid holds ks copies of the
+  // tile set, copy sp accumulating its own slice of the k stages
+  constexpr bool SPLIT = EPI == EPI_F32 && MODE == MGROUP;
+  const int ks = (SPLIT && a.ksplit > 1) ? a.ksplit : 1;
+  const int ntiles_live = (MODE == MGROUP) ? n_mt * a.n_ntiles * ks : (int)gridDim.x;
   if ((int)blockIdx.x >= ntiles_live) return;
-  const int L = xcd_remap(blockIdx.x, ntiles_live);
+  const int L0 = xcd_remap(blockIdx.x, ntiles_live);
+  const int sp = SPLIT ? L0 / (n_mt * a.n_ntiles) : 0;
+  const int L = SPLIT ? L0 - sp * (n_mt * a.n_ntiles) : L0;
   int e, mt, nt;
   {
     const int per_e = (MODE == KGROUP) ? a.n_mtiles * a.n_ntiles : 0x7fffffff;
@@ -269,6 +277,15 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   int nk;
   if constexpr (MODE == MGROUP) nk = (a.K + BK - 1) / BK;
   else nk = (int)((seg_hi - seg_lo + BK - 1) / BK);
+  // this copy's k slice: first stage and end (elements); the whole range
+  // without a split
+  int kofs = 0, kend = a.K;
+  if constexpr (SPLIT) {
+    const int k0 = sp * nk / ks, k1 = (sp + 1) * nk / ks;
+    kofs = k0;
+    kend = min(a.K, k1 * BK);
+    nk = k1 - k0;
+  }
 
   // ---- buffer resources and per-lane load offsets ----------------------
   u32x4 rA, rB;
@@ -323,7 +340,8 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
     const int nrows = (int)(seg_hi - seg_lo);
     if (i < A_PER) {
       if constexpr (ASRC == KC) {
-        la_kc.issue(rA, As, wave, i, kt, a.K);
+        if constexpr (SPLIT) la_kc.issue(rA, As, wave, i, kt + kofs, kend);
+        else la_kc.issue(rA, As, wave, i, kt, a.K);
       } else {
         la_mc.issue(rA, As, wave, i, kt, [&](int k) -> uint32_t {
           return k < nrows ? (uint32_t)k * a.lda * 2 : kOOB;
@@ -332,7 +350,8 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
     } else {
       const int j = i - A_PER;
       if constexpr (BSRC == KC) {
-        lb_kc.issue(rB, Bs, wave, j, kt, a.K);
+        if constexpr (SPLIT) lb_kc.issue(rB, Bs, wave, j, kt + kofs, kend);
+        else lb_kc.issue(rB, Bs, wave, j, kt, a.K);
       } else if constexpr (MODE == MGROUP) {
         lb_mc.issue(rB, Bs, wave, j, kt, [&](int k) -> uint32_t {
           return k < a.K ? (uint32_t)k * a.ldb * 2 : kOOB;
@@ -654,7 +673,7 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   } else if constexpr (EPI == EPI_F32) {
     // fp32 results straight from the accumulators (four consecutive columns
     // per lane and group, 16-byte accesses), written or added to the output
-    float* Cf = a.Cf + (MODE == KGROUP ? (int64_t)e * a.strideC : 0);
+    float* Cf = a.Cf + (MODE == KGROUP ? (int64_t)e * a.strideC : 0) + (int64_t)sp * a.split_stride;
     const int64_t row0 = (MODE == MGROUP) ? m0 : (int64_t)mloc0;
     const int64_t rows_lim = (MODE == MGROUP) ? seg_hi : (int64_t)a.M;
 #pragma unroll
@@ -733,6 +752,81 @@ static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_t
     a.n_ntiles = ntl;
     return launch<CfgWide, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
   }
+}
+
+// Sums the ks fp32 slices of a k-split [M, 2F] gate|up product in slice
+// order, then writes act = [gate | up] and h = silu(gate) * up, both rounded
+// to bf16 from the fp32 sums as the fused epilogue does.  One thread per four
+// consecutive f.
+__global__ void __launch_bounds__(256) split_swiglu_kernel(int64_t M, int F, int ks, int64_t stride,
+                                                           const float* __restrict__ part,
+                                                           uint16_t* __restrict__ act,
+                                                           uint16_t* __restrict__ h) {
+  const int fq = F / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * fq) return;
+  const int64_t m = i / fq;
+  const int f = (int)(i % fq) * 4;
+  const float* pg = part + m * 2 * F + f;
+  f32x4 g = *(const f32x4*)pg, u = *(const f32x4*)(pg + F);
+  for (int sl = 1; sl < ks; ++sl) {
+    g += *(const f32x4*)(pg + sl * stride);
+    u += *(const f32x4*)(pg + sl * stride + F);
+  }
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = g[q] * sigmoid_fast(g[q]) * u[q];
+  *(u32x2*)(h + m * F + f) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  if (act) {
+    *(u32x2*)(act + m * 2 * F + f) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+    *(u32x2*)(act + m * 2 * F + F + f) = u32x2{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
+  }
+}
+
+// Sums the ks fp32 slices of a k-split [M, N] product in slice order and
+// writes the bf16 result.  One thread per four consecutive columns.
+__global__ void __launch_bounds__(256) split_store_kernel(int64_t M, int N, int ks, int64_t stride,
+                                                          const float* __restrict__ part,
+                                                          uint16_t* __restrict__ y) {
+  const int nq = N / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * nq) return;
+  const int64_t m = i / nq;
+  const int n = (int)(i % nq) * 4;
+  const float* p = part + m * N + n;
+  f32x4 v = *(const f32x4*)p;
+  for (int sl = 1; sl < ks; ++sl) v += *(const f32x4*)(p + sl * stride);
+  *(u32x2*)(y + m * N + n) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// Slices of the k range for a dense (one-group) forward product of m_rows
+// rows: when its 128 x 256 tiles fill less than half of the 256 CUs, as many
+// slices as keep tiles x slices within one round of the CUs (at most 8, at
+// least 4 k-stages each); otherwise 1 (no split).
+static int dense_split(int64_t m_rows, int N, int K) {
+  if (m_rows <= 0) return 1;
+  const int64_t tiles =
+      ((m_rows + CfgRows::BM - 1) / CfgRows::BM) * ((N + CfgRows::BN - 1) / CfgRows::BN);
+  if (tiles >= 128) return 1;
+  int ks = (int)(256 / tiles);
+  ks = ks < 8 ? ks : 8;
+  const int nk = (K + CfgRows::BK - 1) / CfgRows::BK;
+  ks = ks < nk / 4 ? ks : nk / 4;
+  return ks < 2 ? 1 : ks;
+}
+
+// k-split fp32 product into the workspace: slice sl of C[M,N] = A[M,K] . B[N,K]^T
+// at ws + sl * M * N
+static hipError_t launch_split_f32(int64_t M, int N, int K, const uint16_t* A, int lda,
+                                   const uint16_t* B, int ldb, int ks, float* ws, hipStream_t s) {
+  Args a = {};
+  a.A = A; a.B = B; a.Cf = ws; a.acc_out = 0;
+  a.m_rows = M; a.N = N; a.K = K; a.F = 0;
+  a.lda = lda; a.ldb = ldb; a.ldc = N; a.strideB = 0; a.G = 1;
+  a.ksplit = ks; a.split_stride = M * (int64_t)N;
+  a.n_mtiles = (int)((M + CfgRows::BM - 1) / CfgRows::BM);
+  a.n_ntiles = (N + CfgRows::BN - 1) / CfgRows::BN;
+  return launch<CfgRows, KC, KC, EPI_F32, MGROUP>(a, a.n_mtiles * a.n_ntiles * ks, s);
 }
 
 }  // namespace gemm
@@ -814,6 +908,39 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.n_mtiles = (2 * F + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (H + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
   return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+}
+
+size_t dense_fwd_split_workspace_bytes(int64_t m_rows, int H, int F) {
+  const int k1 = dense_split(m_rows, 2 * F, H), k2 = dense_split(m_rows, H, F);
+  const size_t b1 = k1 > 1 ? (size_t)k1 * m_rows * 2 * F * sizeof(float) : 0;
+  const size_t b2 = k2 > 1 ? (size_t)k2 * m_rows * H * sizeof(float) : 0;
+  return b1 > b2 ? b1 : b2;
+}
+
+hipError_t launch_dense_gate_up_split(int64_t m_rows, int H, int F, const uint16_t* x,
+                                      const uint16_t* w1, uint16_t* act, uint16_t* h, void* ws,
+                                      hipStream_t s) {
+  const int ks = dense_split(m_rows, 2 * F, H);
+  if (ks == 1)
+    return launch_gemm_gate_up(1, m_rows, H, F, nullptr, nullptr, nullptr, x, w1, act, h, s);
+  hipError_t e = launch_split_f32(m_rows, 2 * F, H, x, H, w1, H, ks, (float*)ws, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = m_rows * (F / 4);
+  hipLaunchKernelGGL(split_swiglu_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m_rows,
+                     F, ks, m_rows * 2 * (int64_t)F, (const float*)ws, act, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_down_split(int64_t m_rows, int H, int F, const uint16_t* h,
+                                   const uint16_t* w2, uint16_t* y, void* ws, hipStream_t s) {
+  const int ks = dense_split(m_rows, H, F);
+  if (ks == 1) return launch_gemm_down(1, m_rows, H, F, nullptr, nullptr, nullptr, h, w2, y, s);
+  hipError_t e = launch_split_f32(m_rows, H, F, h, F, w2, F, ks, (float*)ws, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = m_rows * (H / 4);
+  hipLaunchKernelGGL(split_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m_rows,
+                     H, ks, m_rows * (int64_t)H, (const float*)ws, y);
+  return hipGetLastError();
 }
 
 // C[M,N] (+)= A[M,K] . B[N,K]^T: bf16 operands with K-contiguous rows, fp32

@@ -27,6 +27,12 @@ hipError_t launch_gemm_down(int G, int64_t m_rows, int H, int F, const int32_t* 
                             const int32_t* counts, const int32_t* tile_expert,
                             const uint16_t* h, const uint16_t* w2, uint16_t* y_rows,
                             hipStream_t s);
+size_t dense_fwd_split_workspace_bytes(int64_t m_rows, int H, int F);
+hipError_t launch_dense_gate_up_split(int64_t m_rows, int H, int F, const uint16_t* x,
+                                      const uint16_t* w1, uint16_t* act, uint16_t* h, void* ws,
+                                      hipStream_t s);
+hipError_t launch_dense_down_split(int64_t m_rows, int H, int F, const uint16_t* h,
+                                   const uint16_t* w2, uint16_t* y, void* ws, hipStream_t s);
 hipError_t launch_gemm_dgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
                                   const int32_t* counts, const int32_t* tile_expert,
                                   const uint16_t* dy_rows, const uint16_t* w2,

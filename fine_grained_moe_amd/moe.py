@@ -39,6 +39,9 @@ _SIGS = {
                                       _p, _p]),
     "moe_grouped_gate_up_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_down_fwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_dense_fwd_split_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_dense_gate_up_fwd_split": (_i32, [_i64, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_dense_down_fwd_split": (_i32, [_i64, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
     "moe_combine": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
     "moe_combine_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p]),
     "moe_grouped_swiglu_bwd": (_i32, [_i32, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -251,6 +254,50 @@ def moe_grouped_down_fwd(h, w2, offsets=None, counts=None, tile_expert=None, y_r
                                      _ptr(w2, BF16, "w2"), _ptr(y_rows, BF16, "y_rows"),
                                      _stream()))
     return y_rows
+
+
+def moe_dense_fwd_split_workspace_bytes(m_rows: int, H: int, F: int) -> int:
+    return int(_lib.moe_dense_fwd_split_workspace_bytes(m_rows, H, F))
+
+
+def _split_ws(ws, M, H, F, dev):
+    if ws is None:
+        ws = torch.empty(max(moe_dense_fwd_split_workspace_bytes(M, H, F), 1), dtype=torch.uint8,
+                         device=dev)
+    return ws
+
+
+def moe_dense_gate_up_fwd_split(x, w1, act=True, h=None, ws=None):
+    """Dense gate/up half (one group: the fused shared experts, w1 [1,2F,H])
+    over all rows of x, the contraction split over workgroups when the batch
+    is too small to fill the GPU.  Returns (act, h)."""
+    M, H = x.shape
+    twoF = w1.shape[1]
+    F = twoF // 2
+    dev = x.device
+    if act is True:
+        act = torch.empty((M, 2 * F), dtype=BF16, device=dev)
+    elif act is False:
+        act = None
+    h = torch.empty((M, F), dtype=BF16, device=dev) if h is None else h
+    ws = _split_ws(ws, M, H, F, dev)
+    _expect(w1=(w1, (1, 2 * F, H)), act=(act, (M, 2 * F)), h=(h, (M, F)))
+    _check(_lib.moe_dense_gate_up_fwd_split(M, H, F, _ptr(x, BF16, "x"), _ptr(w1, BF16, "w1"),
+                                            _ptr(act, BF16, "act"), _ptr(h, BF16, "h"), _ptr(ws),
+                                            ws.numel(), _stream()))
+    return act, h
+
+
+def moe_dense_down_fwd_split(h, w2, y=None, ws=None):
+    """Dense down half (w2 [1,H,F]) with the same split.  Returns y."""
+    M, F = h.shape
+    H = w2.shape[1]
+    y = torch.empty((M, H), dtype=BF16, device=h.device) if y is None else y
+    ws = _split_ws(ws, M, H, F, h.device)
+    _expect(w2=(w2, (1, H, F)), y=(y, (M, H)))
+    _check(_lib.moe_dense_down_fwd_split(M, H, F, _ptr(h, BF16, "h"), _ptr(w2, BF16, "w2"),
+                                         _ptr(y, BF16, "y"), _ptr(ws), ws.numel(), _stream()))
+    return y
 
 
 def moe_combine(y_rows, row_of, topk_w, y_shared=None, y=None):
@@ -507,7 +554,9 @@ def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backwar
                                             p["tile_expert"], act=save_for_backward)
     y_sh = act_sh = h_sh = None
     if w1_shf is not None:
-        act_sh, h_sh, y_sh = moe_grouped_swiglu_fwd(x, w1_shf, w2_shf, act=save_for_backward)
+        # the dense product over all tokens: split over k at small batches
+        act_sh, h_sh = moe_dense_gate_up_fwd_split(x, w1_shf, act=save_for_backward)
+        y_sh = moe_dense_down_fwd_split(h_sh, w2_shf)
     y = moe_combine(y_rows, p["row_of"], topk_w, y_sh)
     ctx = dict(x=x, w_router=w_router, w1=w1, w2=w2, w1_shf=w1_shf, w2_shf=w2_shf,
                topk_idx=topk_idx, topk_w=topk_w, topk_s=topk_s, perm=p, act=act, h=h,

@@ -197,6 +197,34 @@ moe_status_t moe_grouped_down_fwd(int32_t G, int64_t m_rows, int32_t H, int32_t 
                                   const uint16_t* w2, uint16_t* y_rows, void* stream);
 
 /*
+ * moe_dense_gate_up_fwd_split / moe_dense_down_fwd_split - the dense (one
+ * group, G = 1, no segments) uses of moe_grouped_gate_up_fwd and
+ * moe_grouped_down_fwd, i.e. the fused shared experts over all m_rows rows of
+ * x (model card: the 2 shared experts are active for every token), for
+ * batches too small to fill the GPU.  Same results as the dense call up to the
+ * order of the fp32 sums: when the product's 128 x 256 tiles would occupy less
+ * than half of the 256 compute units, the contraction (H for gate/up, F for
+ * down) is split into up to 8 slices computed by separate workgroups into fp32
+ * partial products in `ws`, which a second kernel adds in slice order before
+ * the SwiGLU (gate/up: act and h, each rounded to bf16 from the fp32 sums) or
+ * the bf16 store (down).  Otherwise the call runs the dense call itself and
+ * leaves `ws` unused.  Deterministic.
+ *   x [m_rows,H], w1 [2F,H], act [m_rows,2F] (nullable), h [m_rows,F],
+ *   w2 [H,F], y [m_rows,H]; all bf16, row-major.
+ * ws: device workspace of at least moe_dense_fwd_split_workspace_bytes(m_rows,
+ * H, F) bytes (0 when no split is taken; ws may then be NULL), 256-byte
+ * aligned, rewritten by each call; calls sharing one ws must not overlap.
+ * Limits as moe_grouped_gate_up_fwd (H % 64 == 0, F % 32 == 0).
+ */
+size_t moe_dense_fwd_split_workspace_bytes(int64_t m_rows, int32_t H, int32_t F);
+moe_status_t moe_dense_gate_up_fwd_split(int64_t m_rows, int32_t H, int32_t F,
+                                         const uint16_t* x, const uint16_t* w1, uint16_t* act,
+                                         uint16_t* h, void* ws, size_t ws_bytes, void* stream);
+moe_status_t moe_dense_down_fwd_split(int64_t m_rows, int32_t H, int32_t F, const uint16_t* h,
+                                      const uint16_t* w2, uint16_t* y, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/*
  * moe_combine - weighted combine of the routed outputs plus the shared output
  * (model card: 6 routed and 2 shared experts active per token):
  *   y[t,:] = y_shared[t,:] + sum_k topk_w[t,k] * y_rows[row_of[t,k],:]

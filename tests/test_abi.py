@@ -288,3 +288,46 @@ def test_binding_rejects_wrong_shapes():
     with pytest.raises(ValueError, match="dlogit"):
         M.moe_route_dlogit(row_of, torch.empty((T, K), dtype=f32), torch.empty((T, K), dtype=f32),
                            torch.empty((T - 1, E), dtype=f32))
+
+
+def test_dense_split_workspace_and_rejects(lib):
+    """The k-split dense forward halves: a workspace only when the product's
+    128 x 256 tiles fill less than half of the 256 CUs (then 256 // tiles
+    slices, at most 8, at least 4 64-deep k-stages each, fp32 partial products
+    of the larger half); the checks run before any launch."""
+    q = lib.moe_dense_fwd_split_workspace_bytes
+    q.restype = ctypes.c_size_t
+    q.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+
+    def rule(M, H, F):
+        def ks(N, K):
+            tiles = -(-M // 128) * -(-N // 256)
+            if M <= 0 or tiles >= 128:
+                return 1
+            k = min(256 // tiles, 8, -(-K // 64) // 4)
+            return k if k >= 2 else 1
+        k1, k2 = ks(2 * F, H), ks(H, F)
+        return max(k1 * M * 2 * F * 4 if k1 > 1 else 0, k2 * M * H * 4 if k2 > 1 else 0)
+
+    for M, H, F in ((256, 5120, 2816), (8192, 5120, 2816), (200, 1344, 800), (1, 64, 32),
+                    (128, 512, 352), (1024, 5120, 2816), (2048, 5120, 2816), (0, 5120, 2816)):
+        assert q(M, H, F) == rule(M, H, F), (M, H, F)
+    # gate/up: 44 tiles -> 5 slices of [256, 5632]; down: 40 tiles -> 6 slices of [256, 5120]
+    assert q(256, 5120, 2816) == max(5 * 256 * 5632 * 4, 6 * 256 * 5120 * 4)
+    assert q(8192, 5120, 2816) == 0                      # 704 tiles: no split
+    g = lib.moe_dense_gate_up_fwd_split
+    g.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    need = q(256, 5120, 2816)
+    assert g(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), _p(FAKE), need - 1, _p(None)) == 3
+    assert g(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), _p(None), need, _p(None)) == 3
+    assert g(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), _p(FAKE + 16), need, _p(None)) == 1
+    assert g(256, 5120, 2816, _p(None), _p(FAKE), _p(None), _p(FAKE), _p(FAKE), need, _p(None)) == 1
+    assert g(256, 5100, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), _p(FAKE), need, _p(None)) == 2
+    assert g(0, 5120, 2816, _p(None), _p(None), _p(None), _p(None), _p(None), 0, _p(None)) == 0
+    d = lib.moe_dense_down_fwd_split
+    d.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    assert d(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), need - 1, _p(None)) == 3
+    assert d(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), need, _p(None)) == 1
+    assert d(-1, 5120, 2816, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), need, _p(None)) == 1
