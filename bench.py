@@ -36,14 +36,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "dd60b090cf2d5b9a543a4abe10275ceb9112f7fc2064409d1c3162685572bb78"
+TRAFFIC_SOURCE_SHA256 = "93cad6ca9c38af1306bcd0abe959cbdd50d4157bbdb812dac749931001e2dca0"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3082555.8, 405504.0), "down_fwd": (1112652.5, 491525.2),
-    "shared_gate_up_fwd": (348240.3, 135188.8), "shared_down_fwd": (180294.3, 81958.6),
-    "down_dgrad": (1903983.2, 270336.8), "gate_up_dgrad": (2556794.1, 491520.4),
-    "down_wgrad": (321956.6, 1802274.4), "gate_up_wgrad": (847341.4, 3604965.0),
-    "shared_down_dgrad": (352378.3, 90126.7), "shared_gate_up_dgrad": (360522.4, 81920.9),
-    "shared_down_wgrad": (217162.8, 28161.4), "shared_gate_up_wgrad": (434252.0, 56320.6),
+    "gate_up_fwd": (3094534.0, 405504.0), "down_fwd": (1085625.0, 491571.0),
+    "shared_gate_up_fwd": (348246.0, 135199.0), "shared_down_fwd": (180294.0, 81967.0),
+    "down_dgrad": (1920943.0, 270336.0), "gate_up_dgrad": (2565457.0, 491688.0),
+    "down_wgrad": (322471.0, 1802302.0), "gate_up_wgrad": (847564.0, 3605111.0),
+    "shared_down_dgrad": (352381.0, 90124.0), "shared_gate_up_dgrad": (360522.0, 81922.0),
+    "shared_down_wgrad": (217163.0, 28161.0), "shared_gate_up_wgrad": (434252.0, 56321.0),
 }
 
 
