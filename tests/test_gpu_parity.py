@@ -191,6 +191,10 @@ MID = {
     # multiple of 128, F not a multiple of 64
     "T700_H192_E48_K3_F160": Workload("odd", T=700, H=192, E=48, K=3, S=1, F=160, seed=27,
                                       router_std=0.1),
+    # a single routed expert: every token's only choice, combine weight 1, and
+    # the router gradient through the normalised weights vanishes exactly
+    "T333_H128_E1_K1": Workload("e1", T=333, H=128, E=1, K=1, S=1, F=96, seed=28,
+                                router_std=0.1),
 }
 
 
