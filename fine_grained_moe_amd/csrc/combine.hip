@@ -68,7 +68,8 @@ __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
         for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(g[k], v[i], acc[i]);
       }
     }
-    ((u32x4*)(y + (int64_t)t * H))[c] = pack8(acc);
+    // written once and never read back here: streamed past the caches
+    __builtin_nontemporal_store(pack8(acc), (u32x4*)(y + (int64_t)t * H) + c);
   }
 }
 
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
       acc[i] += a0[i];
       acc[4 + i] += a1[i];
     }
-    ((u32x4*)(dx + (int64_t)t * H))[c] = pack8(acc);
+    __builtin_nontemporal_store(pack8(acc), (u32x4*)(dx + (int64_t)t * H) + c);
   }
 }
 

@@ -143,7 +143,10 @@ __global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K,
   const u32x4* src = (const u32x4*)(x + (int64_t)t * H);
   for (int c = lane; c < nchunk; c += 64) {
     u32x4 v = src[c];
-    for (int k = 0; k < K; ++k) ((u32x4*)(x_rows + (int64_t)rows[k] * H))[c] = v;
+    // non-temporal: the K copies of a row do not displace the lines the next
+    // products read (measured: this gather 4 %, the gate/up product after it
+    // 1.6 % faster; the same on the combine backward's scattered rows was slower)
+    for (int k = 0; k < K; ++k) __builtin_nontemporal_store(v, (u32x4*)(x_rows + (int64_t)rows[k] * H) + c);
   }
 }
 
