@@ -38,11 +38,11 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "93cad6ca9c38af1306bcd0abe959cbdd50d4157bbdb812dac749931001e2dca0"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3094534.0, 405504.0), "down_fwd": (1085625.0, 491571.0),
-    "shared_gate_up_fwd": (348246.0, 135199.0), "shared_down_fwd": (180294.0, 81967.0),
-    "down_dgrad": (1920943.0, 270336.0), "gate_up_dgrad": (2565457.0, 491688.0),
-    "down_wgrad": (322471.0, 1802302.0), "gate_up_wgrad": (847564.0, 3605111.0),
-    "shared_down_dgrad": (352381.0, 90124.0), "shared_gate_up_dgrad": (360522.0, 81922.0),
+    "gate_up_fwd": (3065899.0, 405504.0), "down_fwd": (1102603.0, 491521.0),
+    "shared_gate_up_fwd": (348246.0, 135203.0), "shared_down_fwd": (180294.0, 81946.0),
+    "down_dgrad": (1927229.0, 270336.0), "gate_up_dgrad": (2550180.0, 491521.0),
+    "down_wgrad": (321312.0, 1802303.0), "gate_up_wgrad": (847759.0, 3605022.0),
+    "shared_down_dgrad": (352381.0, 90115.0), "shared_gate_up_dgrad": (360522.0, 81921.0),
     "shared_down_wgrad": (217163.0, 28161.0), "shared_gate_up_wgrad": (434252.0, 56321.0),
 }
 
