@@ -41,11 +41,17 @@ bool aligned(uintptr_t a, P... p) {
 #define REQUIRE_WS_ALIGNED(ws) \
   REQUIRE(aligned(256, ws), MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned")
 
+// Widths the kernels address with 32-bit buffer offsets: a row tile of up to
+// 256 rows of H or 2F bf16 values, one expert's weights (4 F H bytes) and the
+// router's re-encoded weight stay well below 4 GiB within these limits.
+constexpr int32_t kMaxWidth = 65536;
+
 moe_status_t check_dims(const char* fn, int32_t T, int32_t H, int32_t E, int32_t K) {
   if (T < 0 || H <= 0 || E <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "T<0 or H,E,K<=0");
   if (K > E) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "K > E");
   if (E > 128 || K > 16) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "E > 128 or K > 16");
   if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H % 64 != 0");
+  if (H > kMaxWidth) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H > 65536");
   if ((int64_t)T * K >= (int64_t)1 << 30) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "T*K too large");
   return MOE_OK;
 }
@@ -106,6 +112,21 @@ size_t moe_route_bwd_dense_workspace_bytes(int32_t T, int32_t H, int32_t E) {
   return moe::route_bwd_dense_workspace_bytes(T, H, E);
 }
 
+moe_status_t moe_permute_check(const int32_t* words) {
+  REQUIRE(words != nullptr, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(words[3] == moe::kPermuteStatusMagic, MOE_ERR_INVALID_ARGUMENT,
+          "not a status block written by moe_permute");
+  const int32_t flags = words[0], n = words[1], first = words[2];
+  if (flags == 0 && n == 0 && first == -1) return MOE_OK;
+  REQUIRE(flags != 0 && (flags & ~3) == 0 && n > 0 && first >= 0, MOE_ERR_INVALID_ARGUMENT,
+          "corrupt status block");
+  snprintf(g_last_error, sizeof(g_last_error),
+           "moe_permute rejected %d token(s), the first being token %d: %s%s%s", n, first,
+           (flags & 1) ? "an expert id outside [0,E)" : "", flags == 3 ? " and " : "",
+           (flags & 2) ? "an expert id repeated within a token" : "");
+  return MOE_ERR_INVALID_ARGUMENT;
+}
+
 moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
                        const float* w_router, const float* bias, int32_t* topk_idx,
                        float* topk_w, float* topk_s, float* scores, void* ws, size_t ws_bytes,
@@ -151,6 +172,8 @@ static moe_status_t check_grouped(const char* fn, int32_t G, int64_t m_rows, int
                                   const int32_t* tile_expert) {
   if (G <= 0 || m_rows < 0 || H <= 0 || F <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, fn, "G,H,F<=0 or m_rows<0");
   if (H % 64 != 0 || F % 32 != 0) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H % 64 or F % 32 != 0");
+  if (H > kMaxWidth || F > kMaxWidth || (int64_t)F * H >= ((int64_t)1 << 30))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "H or F > 65536, or an expert's weights >= 4 GiB");
   if (m_rows >= ((int64_t)1 << 31)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, fn, "m_rows too large");
   const bool dense = offsets == nullptr && counts == nullptr && tile_expert == nullptr;
   const bool grouped = offsets != nullptr && counts != nullptr && tile_expert != nullptr;
@@ -476,9 +499,13 @@ moe_status_t moe_route_bwd_dense(int32_t T, int32_t H, int32_t E, const uint16_t
                                  float* dx_router, int32_t accumulate, void* ws, size_t ws_bytes,
                                  void* stream) {
   REQUIRE(T >= 0 && H > 0 && E > 0, MOE_ERR_INVALID_ARGUMENT, "T<0 or H,E<=0");
-  REQUIRE(E <= 128 && H % 64 == 0, MOE_ERR_UNSUPPORTED_SHAPE, "E > 128 or H % 64 != 0");
-  // the weight gradient addresses each token slice of x with 32-bit offsets
-  REQUIRE(T == 0 || moe::route_bwd_dense_slice_rows(T, H, E) * H * 2 < ((int64_t)1 << 32),
+  REQUIRE(E <= 128 && H % 64 == 0 && H <= kMaxWidth, MOE_ERR_UNSUPPORTED_SHAPE,
+          "E > 128, H % 64 != 0 or H > 65536");
+  // the weight gradient addresses each token slice of its two operands (x
+  // rows, and the three bf16 parts of dlogit side by side: 3 * 128 values a
+  // row at most) with 32-bit offsets
+  REQUIRE(T == 0 || moe::route_bwd_dense_slice_rows(T, H, E) * (H > 384 ? H : 384) * 2 <
+                        ((int64_t)1 << 32),
           MOE_ERR_UNSUPPORTED_SHAPE, "token slice of x >= 4 GiB");
   if (T == 0) {
     // nothing to add; written mode still leaves a (zero) weight gradient

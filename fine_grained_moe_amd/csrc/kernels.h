@@ -13,6 +13,11 @@ hipError_t launch_route(int T, int H, int E, int K, const uint16_t* x, const flo
                         const float* bias, int32_t* topk_idx, float* topk_w, float* topk_s,
                         float* scores, void* ws, hipStream_t s);
 
+// moe_permute's data-check block: the first kPermuteStatusBytes of its
+// workspace, four int32 words (flags, rejected tokens, first rejected token,
+// kPermuteStatusMagic), rewritten by every call
+constexpr size_t kPermuteStatusBytes = 256;
+constexpr int32_t kPermuteStatusMagic = 0x4D4F4550;
 size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
                           const uint16_t* x, int64_t m_cap, int32_t* counts, int32_t* offsets,

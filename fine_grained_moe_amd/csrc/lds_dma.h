@@ -14,10 +14,16 @@ namespace lds {
 // region whose base is wave-uniform (M0); lane l lands at base + 16*l.  The
 // LDS swizzle is therefore applied on the global side: lane l fetches the
 // global chunk that belongs at its LDS slot.  A lane whose element is out of
-// range (rows past the segment, k past K, columns past N) gets an offset past
-// the buffer's num_records, which the hardware turns into zeros (checked per
-// dword), so masked rows and tails contribute exactly nothing.
-constexpr uint32_t kOOB = 0x80000000u;
+// range (rows past the segment, k past K, columns past N) gets the offset
+// kOOB, past the buffer's num_records, which the hardware turns into zeros
+// (checked per dword), so masked rows and tails contribute exactly nothing.
+// kOOB must lie at or above every num_records a resource here is built with:
+// a resource covers whole rows, below 4 GiB in all (the host refuses larger
+// segments), and every row is a multiple of 128 bytes, so num_records is at
+// most 2^32 - 128 < kOOB.  kOOB + 12, the last dword of a 16-byte load, does
+// not wrap in 32 bits.
+constexpr uint32_t kOOB = 0xFFFFFFF0u;
+static_assert(kOOB >= 0xFFFFFF80u && kOOB <= 0xFFFFFFFFu - 12u, "out-of-range offset sentinel");
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 
 // raw buffer resource: base, stride 0, num_records = bytes.  The arguments

@@ -2,8 +2,8 @@
 // tile ("dots.llm1 Technical Report" summary page, "Key claims" and "Method":
 // expert token segments padded to tile multiples; no token is dropped).
 //
-// Integer-only and deterministic (the LDS atomics below only count or set
-// bits, so their order cannot change a result):
+// Integer-only and deterministic (the LDS atomics below only count, set bits
+// or take a minimum, so their order cannot change a result):
 //   1. count   : per 256-token chunk, a histogram of the chunk's expert ids
 //   2. scan    : per expert, exclusive prefix over chunks (chunk bases) and the
 //                total count; padded exclusive scan over experts (offsets)
@@ -12,6 +12,16 @@
 //                tokens with the same expert (popcount of a per-expert token
 //                bitmask), so rows of a segment are in ascending token order
 //   4. rows    : copy each token's x row into its K segment rows (x read once)
+//
+// Data check: a token whose K expert ids are not all in [0,E) and distinct is
+// rejected before any of its ids indexes anything: it is not counted, owns no
+// row, its row_of entries are -1 and its x row is not copied.  count records
+// per chunk what it rejected; scan folds that into the status block at the
+// start of the workspace (written by every call):
+//   [0] flags: bit 0 an id outside [0,E), bit 1 an id repeated in a token
+//   [1] number of rejected tokens
+//   [2] smallest rejected token, -1 if none
+//   [3] kPermuteStatusMagic
 #include "common.h"
 #include "kernels.h"
 
@@ -20,28 +30,87 @@ namespace perm {
 
 constexpr int CH = 256;    // tokens per chunk = threads per workgroup
 constexpr int EMAX = 128;
+constexpr int kNone = 0x7fffffff;
+
+// Loads the K expert ids of one token into ev and checks them: returns 0 if
+// every id lies in [0,E) and no id repeats, else the status flags (bit 0 out
+// of range, bit 1 repeated).
+__device__ __forceinline__ int load_ids(const int32_t* __restrict__ p, int K, int E, int* ev) {
+  int fl = 0;
+  for (int k = 0; k < K; ++k) {
+    const int e = p[k];
+    ev[k] = e;
+    if (e < 0 || e >= E) fl |= 1;
+    for (int j = 0; j < k; ++j)
+      if (ev[j] == e) fl |= 2;
+  }
+  return fl;
+}
 
 __global__ void __launch_bounds__(CH) count_kernel(int T, int E, int K,
                                                    const int32_t* __restrict__ topk_idx,
-                                                   int32_t* __restrict__ chunk_counts) {
+                                                   int32_t* __restrict__ chunk_counts,
+                                                   int32_t* __restrict__ chunk_status) {
   __shared__ int hist[EMAX];
+  __shared__ int bad_flags, bad_count, bad_first;
   const int tid = threadIdx.x, c = blockIdx.x;
   if (tid < EMAX) hist[tid] = 0;
+  if (tid == 0) {
+    bad_flags = 0;
+    bad_count = 0;
+    bad_first = kNone;
+  }
   __syncthreads();
   const int t = c * CH + tid;
-  if (t < T)
-    for (int k = 0; k < K; ++k) atomicAdd(&hist[topk_idx[(int64_t)t * K + k]], 1);
+  if (t < T) {
+    int ev[16];
+    const int fl = load_ids(topk_idx + (int64_t)t * K, K, E, ev);
+    if (fl == 0) {
+      for (int k = 0; k < K; ++k) atomicAdd(&hist[ev[k]], 1);
+    } else {
+      atomicOr(&bad_flags, fl);
+      atomicAdd(&bad_count, 1);
+      atomicMin(&bad_first, t);
+    }
+  }
   __syncthreads();
   if (tid < E) chunk_counts[(int64_t)c * E + tid] = hist[tid];
+  if (tid == 0) {
+    chunk_status[3 * (int64_t)c + 0] = bad_flags;
+    chunk_status[3 * (int64_t)c + 1] = bad_count;
+    chunk_status[3 * (int64_t)c + 2] = bad_first;
+  }
 }
 
 __global__ void __launch_bounds__(EMAX) scan_kernel(int E, int nchunks, int align,
                                                     const int32_t* __restrict__ chunk_counts,
+                                                    const int32_t* __restrict__ chunk_status,
                                                     int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ status) {
   __shared__ int cnt[EMAX];
+  __shared__ int bad_flags, bad_count, bad_first;
   const int tid = threadIdx.x;
+  if (tid == 0) {
+    bad_flags = 0;
+    bad_count = 0;
+    bad_first = kNone;
+  }
+  __syncthreads();
+  {
+    int fl = 0, n = 0, first = kNone;
+    for (int c = tid; c < nchunks; c += EMAX) {
+      fl |= chunk_status[3 * (int64_t)c + 0];
+      n += chunk_status[3 * (int64_t)c + 1];
+      first = min(first, chunk_status[3 * (int64_t)c + 2]);
+    }
+    if (n) {
+      atomicOr(&bad_flags, fl);
+      atomicAdd(&bad_count, n);
+      atomicMin(&bad_first, first);
+    }
+  }
   if (tid < E) {
     // exclusive prefix over chunks; eight independent loads per round
     int run = 0;
@@ -67,6 +136,13 @@ __global__ void __launch_bounds__(EMAX) scan_kernel(int E, int nchunks, int alig
       run += (cnt[e] + align - 1) / align * align;
     }
     offsets[E] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    status[0] = bad_flags;
+    status[1] = bad_count;
+    status[2] = bad_count ? bad_first : -1;
+    status[3] = kPermuteStatusMagic;
   }
 }
 
@@ -110,14 +186,13 @@ __global__ void __launch_bounds__(CH) scatter_kernel(int T, int E, int K,
   const int t = c * CH + tid;
   const int w = tid >> 5, bit = tid & 31;
   int ev[16];
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      ev[k] = topk_idx[(int64_t)t * K + k];
-      atomicOr(&mask[ev[k]][w], 1u << bit);
-    }
-  }
+  const bool ok = t < T && load_ids(topk_idx + (int64_t)t * K, K, E, ev) == 0;
+  if (ok)
+    for (int k = 0; k < K; ++k) atomicOr(&mask[ev[k]][w], 1u << bit);
+  else if (t < T)
+    for (int k = 0; k < K; ++k) row_of[(int64_t)t * K + k] = -1;   // rejected: no rows
   __syncthreads();
-  if (t < T) {
+  if (ok) {
     for (int k = 0; k < K; ++k) {
       const int e = ev[k];
       int rank = __popc(mask[e][w] & ((1u << bit) - 1u));
@@ -136,7 +211,7 @@ __global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K,
                                                    uint16_t* __restrict__ x_rows) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  if (t >= T || row_of[(int64_t)t * K] < 0) return;   // a rejected token owns no rows
   int rows[16];
   for (int k = 0; k < K; ++k) rows[k] = row_of[(int64_t)t * K + k];
   const int nchunk = H / 8;
@@ -152,9 +227,15 @@ __global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K,
 
 }  // namespace perm
 
+// workspace: the 256-byte status block, per-chunk status (3 ints a chunk,
+// rounded up to 256 bytes), per-chunk histograms, per-chunk bases
+static size_t chunk_status_bytes(int nchunks) {
+  return ((size_t)3 * nchunks * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 size_t permute_workspace_bytes(int T, int E) {
   const int nchunks = (T + perm::CH - 1) / perm::CH;
-  return (size_t)2 * nchunks * E * sizeof(int32_t);
+  return kPermuteStatusBytes + chunk_status_bytes(nchunks) + (size_t)2 * nchunks * E * sizeof(int32_t);
 }
 
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
@@ -162,13 +243,15 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
                           int32_t* row_of, int32_t* src_token, int32_t* tile_expert,
                           uint16_t* x_rows, void* ws, hipStream_t s) {
   const int nchunks = (T + perm::CH - 1) / perm::CH;
-  int32_t* chunk_counts = (int32_t*)ws;
+  int32_t* status = (int32_t*)ws;
+  int32_t* chunk_status = (int32_t*)((uint8_t*)ws + kPermuteStatusBytes);
+  int32_t* chunk_counts = (int32_t*)((uint8_t*)chunk_status + chunk_status_bytes(nchunks));
   int32_t* chunk_base = chunk_counts + (size_t)nchunks * E;
   if (nchunks > 0)
     hipLaunchKernelGGL(perm::count_kernel, dim3(nchunks), dim3(perm::CH), 0, s, T, E, K, topk_idx,
-                       chunk_counts);
+                       chunk_counts, chunk_status);
   hipLaunchKernelGGL(perm::scan_kernel, dim3(1), dim3(perm::EMAX), 0, s, E, nchunks, align,
-                     chunk_counts, chunk_base, counts, offsets);
+                     chunk_counts, chunk_status, chunk_base, counts, offsets, status);
   if (m_cap > 0)
     hipLaunchKernelGGL(perm::fill_kernel, dim3((unsigned)((m_cap + 255) / 256)), dim3(256), 0, s, E,
                        align, m_cap, offsets, src_token, tile_expert);

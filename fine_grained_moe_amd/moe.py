@@ -29,6 +29,7 @@ _SIGS = {
     "moe_capacity_rows": (_i64, [_i32, _i32, _i32]),
     "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_permute_check": (_i32, [_p]),
     "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_seq_balance_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_bwd_dense_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -169,7 +170,10 @@ def moe_route(x, w_router, bias, K, topk_idx=None, topk_w=None, topk_s=None, ws=
 
 
 def moe_permute(topk_idx, x, E, m_cap=None, out=None, ws=None):
-    """Returns dict(counts, offsets, row_of, src_token, tile_expert, x_rows)."""
+    """Returns dict(counts, offsets, row_of, src_token, tile_expert, x_rows,
+    status).  status is the call's data-check block (int32 [4], a view of the
+    workspace's first 16 bytes, overwritten by the next call on the same
+    workspace); moe_permute_check(status) decodes it."""
     T, K = topk_idx.shape
     H = x.shape[1]
     A = moe_align()
@@ -193,7 +197,17 @@ def moe_permute(topk_idx, x, E, m_cap=None, out=None, ws=None):
                             _ptr(out["row_of"], I32), _ptr(out["src_token"], I32),
                             _ptr(out["tile_expert"], I32), _ptr(out["x_rows"], BF16),
                             _ptr(ws), ws.numel(), _stream()))
+    out["status"] = ws[:16].view(I32)
     return out
+
+
+def moe_permute_check(status):
+    """Decodes a moe_permute data-check block (int32 [4], on any device; this
+    copies it to the host, so it waits for the call that wrote it).  Raises
+    MoEError naming the rejected tokens, returns None when there are none."""
+    words = status.detach().to("cpu", torch.int32).contiguous()
+    _expect(status=(words, (4,)))
+    _check(_lib.moe_permute_check(words.data_ptr()))
 
 
 def moe_grouped_swiglu_fwd(x_rows, w1, w2, offsets=None, counts=None, tile_expert=None,

@@ -29,10 +29,13 @@
  *     call, so a rejected call has launched nothing.  T == 0 is a valid no-op.
  *   - Outputs are deterministic: the same inputs give bit-identical outputs
  *     (no floating-point atomics anywhere).
- *   - Shape limits: H % 64 == 0, F % 32 == 0, 1 <= K <= E <= 128, K <= 16,
- *     align == moe_align(); row counts below 2^31; for the weight-gradient
- *     entry points m_rows * max(H, 2F) * 2 bytes below 4 GiB (each segment
- *     is addressed with 32-bit offsets; 419,430 rows at H = 5120).
+ *   - Shape limits: H % 64 == 0, F % 32 == 0, H <= 65536, F <= 65536,
+ *     F * H < 2^30 (one expert's weights below 4 GiB), 1 <= K <= E <= 128,
+ *     K <= 16, align == moe_align(); row counts below 2^31; for the
+ *     weight-gradient entry points m_rows * max(H, 2F) * 2 bytes below 4 GiB
+ *     (each segment is addressed with 32-bit buffer offsets, 419,430 rows at
+ *     H = 5120; every admitted segment is read in full and nothing past it).
+ *     Calls outside these limits return MOE_ERR_UNSUPPORTED_SHAPE.
  *
  * Readings of what the pages leave open (all entry points follow them):
  *   scores are sigmoid(logit); the bias is added for selection only; the K
@@ -80,7 +83,8 @@ int64_t moe_capacity_rows(int32_t T, int32_t E, int32_t K);
  * the number of slices of h, depends on T and H).  0 for invalid arguments. */
 size_t moe_route_workspace_bytes(int32_t T, int32_t H, int32_t E);
 
-/* host: bytes of the workspace moe_permute needs. */
+/* host: bytes of the workspace moe_permute needs (at least 256: its first
+ * 16 bytes receive the data-check block, see moe_permute_check). */
 size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
 
 /* host: bytes of the workspace moe_route_bwd needs. */
@@ -140,8 +144,15 @@ moe_status_t moe_route(int32_t T, int32_t H, int32_t E, int32_t K,
  *   x_rows[r,:]    = x[src_token[r],:] for every non-padding row; padding rows
  *                    are left untouched                            [m_cap,H] bf16
  *
- * topk_idx entries must lie in [0,E) and be distinct within a token (as
- * moe_route writes them); other values are undefined behaviour.
+ * Data check (every call): a token whose K ids are not all in [0,E) and
+ * distinct (moe_route always writes such ids) is rejected before any of its
+ * ids indexes memory: it is not counted, owns no row, its row_of entries are
+ * -1 and its x row is not copied; every other token is permuted as above.
+ * The call records what it rejected in the first 16 bytes of ws (four int32:
+ * flags, number of rejected tokens, first rejected token, a marker), which
+ * moe_permute_check decodes after the caller copies them to host memory.  If
+ * any token was rejected, the routing must not be passed on: the other entry
+ * points read topk_idx and row_of without checking them.
  * m_cap must be >= moe_capacity_rows(T,E,K) and a multiple of align.
  * ws: device workspace of at least moe_permute_workspace_bytes(T,E,K) bytes.
  */
@@ -150,6 +161,16 @@ moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t ali
                          int32_t* counts, int32_t* offsets, int32_t* row_of,
                          int32_t* src_token, int32_t* tile_expert, uint16_t* x_rows,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_check - host: decodes moe_permute's data-check block.
+ * words: host copy of the first four int32 of moe_permute's workspace.
+ * Returns MOE_OK when no token was rejected; MOE_ERR_INVALID_ARGUMENT when
+ * some were (moe_last_error() then names the cause: an id outside [0,E), an
+ * id repeated within a token, or both; how many tokens; the first one), or
+ * when the words are not a block moe_permute wrote.  Touches no device state.
+ */
+moe_status_t moe_permute_check(const int32_t* words);
 
 /*
  * moe_grouped_swiglu_fwd - grouped SwiGLU expert FFN over row segments
@@ -236,7 +257,13 @@ moe_status_t moe_combine(int32_t T, int32_t H, int32_t K, const uint16_t* y_rows
                          const uint16_t* y_shared, uint16_t* y, void* stream);
 
 /*
- * moe_combine_bwd - backward of moe_combine:
+ * moe_combine_bwd - backward of moe_combine.  The pages time the layer's
+ * backward (Technical Report summary, "Key claims" and "Results": the grouped
+ * GEMM's forward and backward against Transformer Engine, Table 1) without
+ * defining it; every backward entry point computes the true gradient of its
+ * forward with the routing decision held fixed and no gradient for the
+ * selection bias.  Here, of the combine (model card, "Model Architecture
+ * Features": 6 routed and 2 shared experts per token):
  *   dy_rows[row_of[t,k],:] = topk_w[t,k] * dy[t,:]        (bf16)
  *   dg[t,k]                = <dy[t,:], y_rows[row_of[t,k],:]>   (fp32)
  * Padding rows of dy_rows are not written.
@@ -247,8 +274,12 @@ moe_status_t moe_combine_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dy
                              void* stream);
 
 /*
- * moe_grouped_swiglu_bwd - backward of moe_grouped_swiglu_fwd with the same
- * segment arguments (offsets/counts/tile_expert NULL = dense single group):
+ * moe_grouped_swiglu_bwd - backward of moe_grouped_swiglu_fwd (the backward
+ * the Technical Report summary times, "Results", Table 1; the gradient of the
+ * SwiGLU experts of the aibase news item's architecture paragraph, routing
+ * held fixed) over the same tile-padded segments ("Key claims" / "Method"),
+ * with the same segment arguments (offsets/counts/tile_expert NULL = dense
+ * single group):
  *   dh        = dy_rows . w2[g]                          (per valid row)
  *   dgate     = dh * up * silu'(gate),  silu'(z) = sig(z)(1 + z(1 - sig(z)))
  *   dup       = dh * silu(gate)
@@ -269,8 +300,10 @@ moe_status_t moe_grouped_swiglu_bwd(int32_t G, int64_t m_rows, int32_t H, int32_
                                     void* stream);
 
 /*
- * The four steps of moe_grouped_swiglu_bwd as entry points of their own, same
- * argument meanings; moe_grouped_swiglu_bwd is exactly
+ * The four steps of moe_grouped_swiglu_bwd as entry points of their own (the
+ * grouped GEMM's backward of the Technical Report summary, "Results", Table
+ * 1: data and weight gradients over the tile-padded segments), same argument
+ * meanings; moe_grouped_swiglu_bwd is exactly
  * down_dgrad, gate_up_dgrad, down_wgrad, gate_up_wgrad in that order.  The
  * data gradients and the weight gradients do not depend on each other once
  * dact exists, so a caller may run the weight-gradient steps on another stream.
@@ -302,7 +335,9 @@ moe_status_t moe_grouped_gate_up_wgrad(int32_t G, int64_t m_rows, int32_t H, int
 
 /*
  * moe_route_bwd - backward of moe_route's weights through the selected scores
- * (routing decision held fixed, no bias gradient):
+ * (the FP32 gating of the Technical Report summary, "Method"; the backward is
+ * timed there, "Results", not defined: routing decision held fixed, no bias
+ * gradient):
  *   S_t        = sum_j topk_s[t,j],  g = topk_s / S_t
  *   ds[t,k]    = (dg[t,k] - sum_j g[t,j] dg[t,j]) / S_t
  *   dlogit[t,k]= ds[t,k] * s * (1 - s),   s = topk_s[t,k]
@@ -322,7 +357,10 @@ moe_status_t moe_route_bwd(int32_t T, int32_t H, int32_t E, int32_t K,
                            float* dx_router, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_permute_bwd - un-permute and add every path of the input gradient:
+ * moe_permute_bwd - backward of moe_permute's row gather (the tile-padded
+ * segments of the Technical Report summary, "Key claims" / "Method"; the
+ * backward timed in "Results", routing held fixed): un-permute and add every
+ * path of the input gradient:
  *   dx[t,:] = sum_k dx_rows[row_of[t,k],:] + dx_shared[t,:] + dx_router[t,:]
  * fp32 accumulation, one bf16 rounding.  dx_shared (bf16) and dx_router (fp32)
  * are nullable.

@@ -143,6 +143,9 @@ int main(void) {
   CHECK_HIP(hipMemcpy(hrow, row_of, (size_t)T * K * 4, hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(hsrc, src, (size_t)M * 4, hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(hy, y, (size_t)T * H * 2, hipMemcpyDeviceToHost));
+  int32_t check[4];
+  CHECK_HIP(hipMemcpy(check, pw, sizeof(check), hipMemcpyDeviceToHost));
+  CHECK_MOE(moe_permute_check(check)); /* moe_route's ids: nothing rejected */
 
   int64_t total = 0;
   for (int e = 0; e < E; ++e) {

@@ -66,8 +66,10 @@ def test_host_queries(lib):
     assert lib.moe_route_workspace_bytes(128, 64, 0) == 0
     assert lib.moe_route_workspace_bytes(128, 96, 8) == 0
     assert lib.moe_route_workspace_bytes(-1, 64, 8) == 0
-    assert lib.moe_permute_workspace_bytes(8192, 128, 6) == 2 * 32 * 128 * 4
-    assert lib.moe_permute_workspace_bytes(0, 128, 6) == 0
+    # 256-byte data-check block, per-chunk status (3 int32 per 256-token
+    # chunk, rounded up to 256 bytes), per-chunk histograms and bases
+    assert lib.moe_permute_workspace_bytes(8192, 128, 6) == 256 + 512 + 2 * 32 * 128 * 4
+    assert lib.moe_permute_workspace_bytes(0, 128, 6) == 256
     assert lib.moe_route_bwd_workspace_bytes(8192, 5120, 128, 6) == 128 * 5120 * 4 + 65408 * 4
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
@@ -331,3 +333,91 @@ def test_dense_split_workspace_and_rejects(lib):
     assert d(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), need - 1, _p(None)) == 3
     assert d(256, 5120, 2816, _p(FAKE), _p(FAKE), _p(None), _p(FAKE), need, _p(None)) == 1
     assert d(-1, 5120, 2816, _p(FAKE), _p(FAKE), _p(FAKE), _p(FAKE), need, _p(None)) == 1
+
+
+def test_permute_check_decoder(lib):
+    """moe_permute's data-check block, decoded on the host: flags (bit 0 an id
+    outside [0,E), bit 1 an id repeated within a token), rejected tokens,
+    first rejected token, marker."""
+    f = lib.moe_permute_check
+    f.argtypes = [ctypes.c_void_p]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    MAGIC = 0x4D4F4550
+
+    def call(words):
+        arr = (ctypes.c_int32 * 4)(*words)
+        return f(ctypes.cast(arr, ctypes.c_void_p)), lib.moe_last_error().decode()
+
+    assert call([0, 0, -1, MAGIC])[0] == 0
+    st, msg = call([1, 3, 17, MAGIC])
+    assert st == 1 and "3 token(s)" in msg and "token 17" in msg and "outside [0,E)" in msg
+    assert "repeated" not in msg
+    st, msg = call([2, 1, 0, MAGIC])
+    assert st == 1 and "repeated within a token" in msg and "outside" not in msg
+    st, msg = call([3, 2, 5, MAGIC])
+    assert st == 1 and "outside [0,E) and an expert id repeated" in msg
+    # not a block moe_permute wrote, or an inconsistent one
+    assert call([0, 0, -1, 0])[0] == 1 and "not a status block" in lib.moe_last_error().decode()
+    for words in ([4, 1, 0, MAGIC], [1, 0, -1, MAGIC], [0, 2, 3, MAGIC], [1, 1, -1, MAGIC]):
+        st, msg = call(words)
+        assert st == 1 and "corrupt" in msg, words
+    assert f(None) == 1
+
+
+def _oob_sentinel():
+    src = open(os.path.join(ROOT, "fine_grained_moe_amd", "csrc", "lds_dma.h")).read()
+    return int(re.search(r"constexpr uint32_t kOOB = (0x[0-9A-Fa-f]+)u;", src).group(1), 16)
+
+
+def _largest_admitted(call, lo, hi):
+    """Largest n in [lo, hi) that `call(n)` admits (returns 1: the shape
+    passed and the null pointers were refused) when every larger one is
+    refused as an unsupported shape (2)."""
+    assert call(lo) == 1 and call(hi) == 2
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if call(mid) == 1:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
+def test_out_of_range_offset_above_every_buffer(lib):
+    """The grouped GEMMs send masked rows, columns and k past a buffer to the
+    offset kOOB, which must read as zeros: it must lie at or above the byte
+    size (num_records) of every buffer resource the kernels build, at the
+    largest shapes the host checks admit, and a 16-byte load there must not
+    wrap in 32 bits.  The model below lists each resource's byte size."""
+    kOOB = _oob_sentinel()
+    assert kOOB + 12 < 1 << 32
+    sizes = {}
+    # K-grouped weight gradients: one resource per operand over a whole
+    # segment of rows (dense call: m_rows rows), rows of H or 2F bf16 values
+    for name in ("moe_grouped_down_wgrad", "moe_grouped_gate_up_wgrad"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 7
+        for H, F in ((5120, 1408), (64, 32), (65536, 32), (128, 65536), (8192, 65536 // 64 * 32)):
+            n = _largest_admitted(lambda m: f(1, m, H, F, *[_p(None)] * 7), 1, 1 << 31)
+            sizes[f"{name} segment, H={H} F={F}"] = n * max(H, 2 * F) * 2
+    # row-grouped products: a row tile (up to 256 rows) of the row operand, one
+    # expert's weight matrix, the act tile of the SwiGLU-backward epilogue
+    g = lib.moe_grouped_gate_up_fwd
+    g.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 8
+    Hmax = _largest_admitted(lambda h: g(1, 1, h * 64, 32, *[_p(None)] * 8), 1, 1 << 20) * 64
+    Fmax = _largest_admitted(lambda fq: g(1, 1, 64, fq * 32, *[_p(None)] * 8), 1, 1 << 20) * 32
+    assert Hmax == 65536 and Fmax == 65536
+    FH = _largest_admitted(lambda fq: g(1, 1, 65536, fq * 32, *[_p(None)] * 8), 1, 2048) * 32 * 65536
+    sizes["row tile"] = 256 * max(Hmax, 2 * Fmax) * 2
+    sizes["expert weights"] = 2 * FH * 2
+    sizes["act tile"] = 128 * 2 * Fmax * 2
+    # router: a 128-token tile of x, the three bf16 parts of the weight
+    r = lib.moe_route
+    r.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]
+    Hr = _largest_admitted(lambda h: r(1, h * 64, 8, 2, *[_p(None)] * 8, 0, _p(None)), 1, 1 << 20) * 64
+    sizes["router x tile"] = 128 * Hr * 2
+    sizes["router weight parts"] = 3 * 128 * Hr * 2
+    for k, v in sizes.items():
+        assert 0 < v <= (1 << 32) - 128 <= kOOB, (k, v)
+    # the dots.llm1 limit: 419,430 rows of 10 KB are admitted, one more is not
+    assert sizes["moe_grouped_gate_up_wgrad segment, H=5120 F=1408"] == 419430 * 10240

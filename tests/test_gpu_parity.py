@@ -14,6 +14,7 @@ import pytest
 from fine_grained_moe_amd.synthetic import (EP_SHARD, WORKLOADS, Workload, generate_numpy,
                                             generate_shard_torch, generate_torch)
 from oracle import moe_oracle as O
+import bf16_pipeline as B
 import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -35,11 +36,14 @@ ALIGN = 128
 
 @pytest.fixture(autouse=True)
 def _report():
-    """Print every comparison's errors (inf-norm, 2-norm, element-wise)."""
+    """Print every comparison's errors: element-wise against the oracle,
+    2-norm, and (where the bf16-storage pipeline is compared) that pipeline's
+    own element-wise error and the kernels' error against it."""
     P.REPORT.clear()
     yield
-    for name, e, n, el in P.REPORT:
-        print(f"  {name:40s} max {e:.2e}  norm {n:.2e}  elementwise {el:.2e}", flush=True)
+    for name, e, n, e_emu, e_kern in P.REPORT:
+        extra = "" if e_emu is None else f"  storage {e_emu:.2e}  kernel {e_kern:.2e}"
+        print(f"  {name:40s} elementwise {e:.2e}  norm {n:.2e}{extra}", flush=True)
 
 
 class LazyExperts:
@@ -82,7 +86,13 @@ def run_layer(M, g, K, backward):
 
 
 def full_layer_checks(M, inp, K, backward=True, label=""):
-    """Every stage and the whole layer against the full oracle (small layers)."""
+    """Every stage and the whole layer against the full oracle (small layers).
+
+    Stage checks feed the oracle the GPU's own inputs of that stage (its
+    routing, rows, upstream gradient rows), so that each kernel is checked
+    alone; the bf16-storage pipeline (exact arithmetic, bf16 stores) runs on
+    the GPU's routing and gives the widened bound where bf16 storage alone
+    exceeds the tolerance (see tests/parity.py)."""
     E = inp["w1"].shape[0]
     S = inp["w1_sh"].shape[0]
     g = to_gpu(inp)
@@ -98,7 +108,12 @@ def full_layer_checks(M, inp, K, backward=True, label=""):
     ref_perm = O.permute(idx, E, ALIGN)
     P.check_permute(p, ref_perm, E, ALIGN, m_cap)
     valid = p["src_token"] >= 0
+    nv = int(p["offsets"][E])
     assert np.array_equal(p["x_rows"][valid], inp["x"][p["src_token"][valid]]), "x_rows"
+    # the bf16-storage pipeline on the GPU's routing
+    gpu_route = dict(topk_idx=idx, topk_w=P.to_np(ctx["topk_w"]), topk_s=P.to_np(ctx["topk_s"]))
+    emu = B.layer(inp, K, ALIGN, dy=inp["dy"] if backward else None, route=gpu_route)
+    ev = emu["perm"]["src_token"] >= 0   # the same rows as `valid`, cut at offsets[E]
     # experts, on the GPU's own rows
     x_rows = p["x_rows"]
     act, hid, y_rows = O.experts_forward(x_rows, inp["w1"], inp["w2"], p["offsets"], p["counts"])
@@ -128,18 +143,20 @@ def full_layer_checks(M, inp, K, backward=True, label=""):
     # expert backward, on the GPU's own rows and upstream rows
     dx_rows_ref, dW1_ref, dW2_ref, dact_ref = O.experts_backward(
         x_rows, inp["w1"], inp["w2"], act, P.to_np(grads["dy_rows"]), p["offsets"], p["counts"])
-    P.assert_close(f"{label} dact", P.to_np(grads["dact"])[valid], dact_ref[valid])
-    P.assert_close(f"{label} dx_rows", P.to_np(grads["dx_rows"])[valid], dx_rows_ref[valid])
-    P.per_slice_close(f"{label} dW1", P.to_np(grads["dw1"]), dW1_ref)
-    P.per_slice_close(f"{label} dW2", P.to_np(grads["dw2"]), dW2_ref)
+    P.assert_close(f"{label} dact", P.to_np(grads["dact"])[valid], dact_ref[valid],
+                   emu["dact"][:nv][ev])
+    P.assert_close(f"{label} dx_rows", P.to_np(grads["dx_rows"])[valid], dx_rows_ref[valid],
+                   emu["dx_rows"][:nv][ev])
+    P.per_slice_close(f"{label} dW1", P.to_np(grads["dw1"]), dW1_ref, emu["dW1"])
+    P.per_slice_close(f"{label} dW2", P.to_np(grads["dw2"]), dW2_ref, emu["dW2"])
     if S > 0:
         dW1s, dW2s = unfuse_shared(P.to_np(grads["dw1_sh"])[0], P.to_np(grads["dw2_sh"])[0], S)
         for s in range(S):
             a, _, _ = O.expert_ffn(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s])
             _, dw1r, dw2r, _ = O.expert_ffn_bwd(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s], a, dy)
-            P.assert_close(f"{label} dW1_sh[{s}]", dW1s[s], dw1r)
-            P.assert_close(f"{label} dW2_sh[{s}]", dW2s[s], dw2r)
-    # router backward, on the GPU's own routing and dg
+            P.assert_close(f"{label} dW1_sh[{s}]", dW1s[s], dw1r, emu["dW1_sh"][s])
+            P.assert_close(f"{label} dW2_sh[{s}]", dW2s[s], dw2r, emu["dW2_sh"][s])
+    # router backward, on the GPU's own routing and dg (fp32 sums of fp32 inputs)
     dWr_ref, dxr_ref, _ = O.router_bwd(inp["x"], inp["w_router"], idx, P.to_np(ctx["topk_s"]),
                                         P.to_np(grads["dg"]))
     P.assert_close(f"{label} dW_r", P.to_np(grads["dw_router"]), dWr_ref)
@@ -154,9 +171,10 @@ def full_layer_checks(M, inp, K, backward=True, label=""):
     ref_bwd = O.backward(inp, ref_fwd, dy)
     P.assert_close(f"{label} dx", P.to_np(grads["dx"])[same], ref_bwd["dx"][same])
     if same.all():
-        P.per_slice_close(f"{label} dW1 (e2e)", P.to_np(grads["dw1"]), ref_bwd["dW1"])
-        P.per_slice_close(f"{label} dW2 (e2e)", P.to_np(grads["dw2"]), ref_bwd["dW2"])
-        P.assert_close(f"{label} dW_r (e2e)", P.to_np(grads["dw_router"]), ref_bwd["dW_r"])
+        P.per_slice_close(f"{label} dW1 (e2e)", P.to_np(grads["dw1"]), ref_bwd["dW1"], emu["dW1"])
+        P.per_slice_close(f"{label} dW2 (e2e)", P.to_np(grads["dw2"]), ref_bwd["dW2"], emu["dW2"])
+        P.assert_close(f"{label} dW_r (e2e)", P.to_np(grads["dw_router"]), ref_bwd["dW_r"],
+                       emu["dW_r"])
     return dict(n_diff=n_diff, n_tie=n_tie)
 
 
@@ -289,6 +307,47 @@ def test_empty_batch(M):
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
 
 
+def test_permute_rejects_bad_ids(M):
+    """The permutation's data check: tokens with an expert id outside [0,E)
+    (too large, negative) or repeated within the token are rejected before
+    any id indexes memory (no rows, row_of -1, x row not copied) and reported
+    in the status block; every other token is permuted exactly as the oracle
+    permutes the valid tokens alone.  A second call with valid ids on the same
+    workspace reports nothing."""
+    T, H, E, K = 700, 128, 16, 4
+    rng = np.random.default_rng(91)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    bad = {5: (2, E), 6: (0, -1), 300: (1, 1 << 30), 301: (3, None), 699: (0, None)}
+    for t, (k, v) in bad.items():
+        idx[t, k] = idx[t, (k + 1) % K] if v is None else v   # None: repeat another id
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    ws = torch.empty(M.moe_permute_workspace_bytes(T, E, K), dtype=torch.uint8, device=DEV)
+    print(f"case: permute with {len(bad)} bad tokens, T {T} E {E} K {K}", flush=True)
+    p = M.moe_permute(torch.from_numpy(idx).to(DEV), x, E, ws=ws)
+    torch.cuda.synchronize()
+    st = P.to_np(p["status"])
+    assert st[0] == 3 and st[1] == len(bad) and st[2] == 5, st
+    with pytest.raises(M.MoEError, match="rejected 5 token"):
+        M.moe_permute_check(p["status"])
+    good = np.array([t for t in range(T) if t not in bad])
+    ref = O.permute(idx[good], E, ALIGN)
+    g = {k: P.to_np(v) for k, v in p.items() if k not in ("x_rows", "status")}
+    assert np.array_equal(g["counts"], ref["counts"]) and np.array_equal(g["offsets"], ref["offsets"])
+    assert np.array_equal(g["row_of"][good], ref["row_of"])
+    assert (g["row_of"][sorted(bad)] == -1).all()
+    total = int(ref["offsets"][E])
+    want_src = np.where(ref["src_token"] >= 0, good[np.maximum(ref["src_token"], 0)], -1)
+    assert np.array_equal(g["src_token"][:total], want_src) and (g["src_token"][total:] == -1).all()
+    rows = torch.from_numpy(ref["row_of"].reshape(-1)).to(DEV).long()
+    toks = torch.from_numpy(np.repeat(good, K)).to(DEV).long()
+    assert torch.equal(p["x_rows"][rows], x[toks])
+    # valid ids on the same workspace: the block is rewritten, nothing rejected
+    ok = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    p2 = M.moe_permute(torch.from_numpy(ok).to(DEV), x, E, ws=ws)
+    M.moe_permute_check(p2["status"])
+    assert P.to_np(p2["status"]).tolist()[:3] == [0, 0, -1]
+
+
 def test_route_special_values(M):
     """Tokens with a NaN input (every logit NaN, ranked lowest: experts 0..K-1
     in index order, NaN weights), all-zero tokens (every score exactly 1/2, so
@@ -320,7 +379,35 @@ def test_route_special_values(M):
 # ---------------------------------------------------------------------------
 # full dots.llm1-shaped workloads (the benchmark's launch configuration)
 # ---------------------------------------------------------------------------
-def sampled_checks(M, w, backward, n_tokens=12, seed=0):
+def pick_experts(counts, n, rng):
+    """The smallest and the largest non-empty expert, the median one by
+    count, then random non-empty experts up to n (sorted, distinct)."""
+    nonempty = np.nonzero(counts)[0]
+    by_count = nonempty[np.argsort(counts[nonempty], kind="stable")]
+    pick = {int(by_count[0]), int(by_count[-1]), int(by_count[len(by_count) // 2])}
+    rest = [int(e) for e in rng.permutation(nonempty) if int(e) not in pick]
+    return sorted(pick | set(rest[:max(0, n - len(pick))]))
+
+
+def unit_wgrad_checks(name, x_all, dy_all, w1e, w2e, dw1, dw2, units):
+    """Weight gradients of single hidden units over all of an expert's rows:
+    gate row f and up row F+f of dW1 and column f of dW2 depend on unit f
+    alone (its two W1 rows and its W2 column).  x_all, dy_all: the expert's
+    rows (fp32 arrays); dw1 [2F,H], dw2 [H,F]: the GPU's gradients (torch)."""
+    F = w1e.shape[0] // 2
+    for f in units:
+        w1u = w1e[[f, F + f]]
+        w2u = w2e[:, [f]]
+        au, _, _ = O.expert_ffn(x_all, w1u, w2u)
+        _, dw1u, dw2u, _ = O.expert_ffn_bwd(x_all, w1u, w2u, au, dy_all)
+        ae, he, _ = B.expert_forward(x_all, w1u, w2u)
+        _, dw1e, dw2e, _ = B.expert_backward(x_all, w1u, w2u, ae, he, dy_all)
+        P.assert_close(f"{name} dW1[{f}] gate", P.to_np(dw1[f]), dw1u[0], dw1e[0])
+        P.assert_close(f"{name} dW1[{F + f}] up", P.to_np(dw1[F + f]), dw1u[1], dw1e[1])
+        P.assert_close(f"{name} dW2[:,{f}]", P.to_np(dw2[:, f]), dw2u[:, 0], dw2e[:, 0])
+
+
+def sampled_checks(M, w, backward, n_tokens=12, n_experts=4, n_units=3, seed=0):
     g = generate_torch(w, DEV, with_dy=backward)
     K, E, S = w.K, w.E, w.S
     y, ctx, grads = run_layer(M, g, K, backward)
@@ -341,24 +428,25 @@ def sampled_checks(M, w, backward, n_tokens=12, seed=0):
     vmask = src >= 0
     assert torch.equal(ctx["perm"]["x_rows"][vmask], g["x"][src[vmask]]), "x_rows"
 
-    # whole expert segments of sampled experts (stage-wise, GPU rows)
+    # rows of sampled experts, stage by stage on the GPU's own rows (a random
+    # subset of 2048 rows of a longer segment: each row's result depends on
+    # that row alone)
     counts = p["counts"]
-    nonempty = np.nonzero(counts)[0]
-    pick = sorted({int(nonempty[0]), int(nonempty[-1]), int(nonempty[len(nonempty) // 2]),
-                   int(np.argmax(counts))})
     rng = np.random.default_rng(seed)
+    pick = pick_experts(counts, n_experts, rng)
+    print(f"  {w.name}: sampled experts {pick} with {[int(counts[e]) for e in pick]} rows", flush=True)
+    row_sets = {}
     for e in pick:
         r0, n = int(p["offsets"][e]), int(counts[e])
-        if n > 2048:  # bound host work on giant segments: a random row subset
-            rows = np.sort(rng.choice(n, 2048, replace=False)) + r0
-        else:
-            rows = np.arange(r0, r0 + n)
-        xr = P.to_np(ctx["perm"]["x_rows"][torch.from_numpy(rows).to(DEV)])
-        a, hid, ye = O.expert_ffn(xr, W1[e], W2[e])
+        rows = np.sort(rng.choice(n, 2048, replace=False)) + r0 if n > 2048 else np.arange(r0, r0 + n)
+        row_sets[e] = rows
         sel = torch.from_numpy(rows).to(DEV)
+        xr = P.to_np(ctx["perm"]["x_rows"][sel])
+        a, hid, ye = O.expert_ffn(xr, W1[e], W2[e])
         P.assert_close(f"{w.name} act[e={e}]", P.to_np(ctx["act"][sel]), a)
         P.assert_close(f"{w.name} h[e={e}]", P.to_np(ctx["h"][sel]), hid)
-        P.assert_close(f"{w.name} y_rows[e={e}]", P.to_np(ctx["y_rows"][sel]), ye)
+        _, _, y_e = B.expert_forward(xr, W1[e], W2[e])
+        P.assert_close(f"{w.name} y_rows[e={e}]", P.to_np(ctx["y_rows"][sel]), ye, y_e)
 
     # sampled tokens end to end (routing agreeing)
     toks = np.sort(rng.choice(w.T, n_tokens, replace=False))
@@ -374,26 +462,32 @@ def sampled_checks(M, w, backward, n_tokens=12, seed=0):
     P.assert_close(f"{w.name} dx[sampled]", P.to_np(grads["dx"])[toks][same], ref_b["dx"][same])
     P.assert_close(f"{w.name} dg[sampled]", P.to_np(grads["dg"])[toks][same], ref_b["dg"][same])
 
-    # expert weight gradients of sampled experts (stage-wise, GPU upstream rows)
-    for e in pick[:3]:
-        r0, n = int(p["offsets"][e]), int(counts[e])
-        if n > 4096:
-            continue
-        sel = torch.arange(r0, r0 + n, device=DEV)
+    # backward of the sampled experts on the GPU's own upstream rows: dact and
+    # dx_rows on the sampled rows, the weight gradients of sampled hidden
+    # units over every row of the expert (however long the segment)
+    F = w.F
+    for e in pick:
+        rows = row_sets[e]
+        sel = torch.from_numpy(rows).to(DEV)
         xr = P.to_np(ctx["perm"]["x_rows"][sel])
+        dyr = P.to_np(grads["dy_rows"][sel])
         a, _, _ = O.expert_ffn(xr, W1[e], W2[e])
-        dxr, dw1r, dw2r, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, P.to_np(grads["dy_rows"][sel]))
-        P.assert_close(f"{w.name} dact[e={e}]", P.to_np(grads["dact"][sel]), dar)
-        P.assert_close(f"{w.name} dx_rows[e={e}]", P.to_np(grads["dx_rows"][sel]), dxr)
-        P.assert_close(f"{w.name} dW1[e={e}]", P.to_np(grads["dw1"][e]), dw1r)
-        P.assert_close(f"{w.name} dW2[e={e}]", P.to_np(grads["dw2"][e]), dw2r)
+        dxr, _, _, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, dyr)
+        ae, he, _ = B.expert_forward(xr, W1[e], W2[e])
+        dx_e, _, _, dact_e = B.expert_backward(xr, W1[e], W2[e], ae, he, dyr)
+        P.assert_close(f"{w.name} dact[e={e}]", P.to_np(grads["dact"][sel]), dar, dact_e)
+        P.assert_close(f"{w.name} dx_rows[e={e}]", P.to_np(grads["dx_rows"][sel]), dxr, dx_e)
+        r0, n = int(p["offsets"][e]), int(counts[e])
+        all_rows = torch.arange(r0, r0 + n, device=DEV)
+        unit_wgrad_checks(f"{w.name} e={e} ({n} rows)", P.to_np(ctx["perm"]["x_rows"][all_rows]),
+                          P.to_np(grads["dy_rows"][all_rows]), W1[e], W2[e], grads["dw1"][e],
+                          grads["dw2"][e], rng.choice(F, n_units, replace=False))
     empty = np.nonzero(counts == 0)[0]
     if len(empty):
         assert not grads["dw1"][torch.from_numpy(empty).to(DEV)].any()
         assert not grads["dw2"][torch.from_numpy(empty).to(DEV)].any()
 
     # shared experts: sampled hidden units (each unit's gradient depends on it alone)
-    F = w.F
     dw1f = grads["dw1_sh"][0]
     dw2f = grads["dw2_sh"][0]
     for s in range(S):
@@ -402,10 +496,13 @@ def sampled_checks(M, w, backward, n_tokens=12, seed=0):
             w2u = W2s[s][:, [f]]
             au, _, _ = O.expert_ffn(x, w1u, w2u)
             _, dw1u, dw2u, _ = O.expert_ffn_bwd(x, w1u, w2u, au, dy)
+            ae, he, _ = B.expert_forward(x, w1u, w2u)
+            _, dw1e, dw2e, _ = B.expert_backward(x, w1u, w2u, ae, he, dy)
             gate_row, up_row = s * F + f, S * F + s * F + f
-            P.assert_close(f"{w.name} dW1_sh[{s},{f}] gate", P.to_np(dw1f[gate_row]), dw1u[0])
-            P.assert_close(f"{w.name} dW1_sh[{s},{f}] up", P.to_np(dw1f[up_row]), dw1u[1])
-            P.assert_close(f"{w.name} dW2_sh[{s},{f}]", P.to_np(dw2f[:, s * F + f]), dw2u[:, 0])
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] gate", P.to_np(dw1f[gate_row]), dw1u[0], dw1e[0])
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] up", P.to_np(dw1f[up_row]), dw1u[1], dw1e[1])
+            P.assert_close(f"{w.name} dW2_sh[{s},{f}]", P.to_np(dw2f[:, s * F + f]), dw2u[:, 0],
+                           dw2e[:, 0])
 
     # router gradient, full, on the GPU's own routing and dg
     dWr_ref, _, _ = O.router_bwd(x, wr, idx, P.to_np(ctx["topk_s"]), P.to_np(grads["dg"]))
@@ -428,12 +525,14 @@ def test_prefill_sampled(M):
 
 @pytest.mark.timeout(600)
 def test_skew_sampled(M):
-    sampled_checks(M, WORKLOADS["skew"], backward=True)
+    """The skewed batch: its largest segments hold thousands of rows (512
+    k-stages per weight-gradient tile), compared over all of their rows."""
+    sampled_checks(M, WORKLOADS["skew"], backward=True, n_experts=5)
 
 
 @pytest.mark.timeout(600)
 def test_fwdbwd_sampled(M):
-    sampled_checks(M, WORKLOADS["fwdbwd"], backward=True)
+    sampled_checks(M, WORKLOADS["fwdbwd"], backward=True, n_experts=8, n_units=2)
 
 
 # The largest token count a training step accepts at dots shapes: the weight
@@ -482,25 +581,52 @@ def test_ep_shard_sampled(M):
         rows = np.sort(rng.choice(R, 256, replace=False)) + e * R
         sel = torch.from_numpy(rows).to(DEV)
         xr = P.to_np(g["x_rows"][sel])
+        dyr = P.to_np(g["dy_rows"][sel])
         a, hid, ye = O.expert_ffn(xr, W1[e], W2[e])
+        ae, he, y_e = B.expert_forward(xr, W1[e], W2[e])
         P.assert_close(f"shard act[e={e}]", P.to_np(act[sel]), a)
         P.assert_close(f"shard h[e={e}]", P.to_np(h[sel]), hid)
-        P.assert_close(f"shard y_rows[e={e}]", P.to_np(y_rows[sel]), ye)
-        dxr, _, _, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, P.to_np(g["dy_rows"][sel]))
-        P.assert_close(f"shard dact[e={e}]", P.to_np(dact[sel]), dar)
-        P.assert_close(f"shard dx_rows[e={e}]", P.to_np(dx_rows[sel]), dxr)
+        P.assert_close(f"shard y_rows[e={e}]", P.to_np(y_rows[sel]), ye, y_e)
+        dxr, _, _, dar = O.expert_ffn_bwd(xr, W1[e], W2[e], a, dyr)
+        dx_e, _, _, dact_e = B.expert_backward(xr, W1[e], W2[e], ae, he, dyr)
+        P.assert_close(f"shard dact[e={e}]", P.to_np(dact[sel]), dar, dact_e)
+        P.assert_close(f"shard dx_rows[e={e}]", P.to_np(dx_rows[sel]), dxr, dx_e)
         # weight gradients of sampled hidden units over all of the expert's rows
         all_rows = torch.arange(e * R, (e + 1) * R, device=DEV)
-        xa = P.to_np(g["x_rows"][all_rows])
-        dya = P.to_np(g["dy_rows"][all_rows])
-        for f in rng.choice(F, 2, replace=False):
-            w1u = W1[e][[f, F + f]]
-            w2u = W2[e][:, [f]]
-            au, _, _ = O.expert_ffn(xa, w1u, w2u)
-            _, dw1u, dw2u, _ = O.expert_ffn_bwd(xa, w1u, w2u, au, dya)
-            P.assert_close(f"shard dW1[{e},{f}] gate", P.to_np(dw1[e, f]), dw1u[0])
-            P.assert_close(f"shard dW1[{e},{f}] up", P.to_np(dw1[e, F + f]), dw1u[1])
-            P.assert_close(f"shard dW2[{e}][:,{f}]", P.to_np(dw2[e][:, f]), dw2u[:, 0])
+        unit_wgrad_checks(f"shard e={e}", P.to_np(g["x_rows"][all_rows]),
+                          P.to_np(g["dy_rows"][all_rows]), W1[e], W2[e], dw1[e], dw2[e],
+                          rng.choice(F, 2, replace=False))
+
+
+@pytest.mark.timeout(600)
+def test_wgrad_segment_past_2gib(M):
+    """A dense gate/up weight gradient over one segment of 400,001 rows at
+    H = 5120, F = 1408: both operands exceed 2 GiB (dact 2.25 GB, x rows
+    4.1 GB; below the 4 GiB the ABI admits), and 400,001 is not a multiple of
+    the 32-row k-stage, so the last stage holds 31 rows past the segment's
+    end.  Those rows must read as zeros: their buffer offset lies past every
+    admissible segment size.  Checked on sampled hidden units over all rows."""
+    n, H, F = 400_001, 5120, 1408
+    print(f"case: dense gate/up wgrad, {n} rows, H {H}, F {F}", flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(404)
+    x_rows = torch.randn((n, H), generator=gen, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    dact = torch.empty((n, 2 * F), dtype=torch.bfloat16, device=DEV)
+    for i in range(0, n, 65536):   # bounded fp32 staging
+        m = min(65536, n - i)
+        dact[i:i + m] = torch.randn((m, 2 * F), generator=gen, device=DEV).to(torch.bfloat16)
+    assert n * 2 * F * 2 > 1 << 31 and n * H * 2 > 1 << 31 and n * H * 2 < 1 << 32
+    dw1 = M.moe_grouped_gate_up_wgrad(dact, x_rows, 1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(404)
+    for f in sorted(rng.choice(2 * F, 4, replace=False)):
+        col = dact[:, f].float()
+        ref = np.zeros(H, np.float64)
+        for i in range(0, n, 65536):   # fp64 sum over all rows, in row blocks
+            m = min(65536, n - i)
+            ref += P.to_np(col[i:i + m]).astype(np.float64) @ P.to_np(x_rows[i:i + m]).astype(np.float64)
+        got = P.to_np(dw1[0, f])
+        P.assert_close(f"dW1[{f}] over {n} rows", got, ref)
 
 
 def test_inference_forward_without_saved_activations(M):
