@@ -6,7 +6,11 @@ dots.llm1 shapes (H=5120, 128 routed experts of width 1408, top-6, 2 shared
 experts), synthetic seeded inputs resident in HBM.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload fwdbwd|prefill|decode|skew|ep_shard]
-                    [--no-cpu-baseline] [--no-balance] [--no-graph] [--copy-calibration]
+                    [--no-cpu-baseline] [--cpu-seconds S] [--no-configs] [--no-balance]
+                    [--no-graph] [--copy-calibration]
+
+The default fwd+bwd run also times the forward of the decode (T=256), prefill
+(T=8192) and skewed (T=16384) configurations ("configs" in the JSON line).
 """
 from __future__ import annotations
 
@@ -91,8 +95,11 @@ def parse():
                     help="ep_shard: the grouped expert products alone (fwd+bwd) at one GPU's "
                          "share of an 8-way expert-parallel layer, 16 experts x 3072 rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
-                    help="tokens of the same batch the CPU oracle runs on")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="about how long the timed CPU oracle run takes (its token count is "
+                         "sized to this)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward timings of the decode, prefill and skewed configurations")
     ap.add_argument("--no-balance", action="store_true",
                     help="skip the timing of the step with load balancing")
     ap.add_argument("--no-graph", action="store_true",
@@ -356,39 +363,54 @@ def gemm_launch_bytes(w, name, live=None):
     return rows * 2 * F * 2 + rows * H * 2 + wt              # dact, x rows; dW1
 
 
-class LazyExperts:
-    """Per-expert fp32 view of a host bf16 tensor [E, R, C] for the oracle."""
-
-    def __init__(self, t):
-        self.t = t.detach().to("cpu")
-        self.shape = tuple(self.t.shape)
-
-    def __getitem__(self, e):
-        return self.t[e].float().numpy()
+def _elementwise_err(a, r):
+    """max_i |a_i - r_i| / max(|r_i|, rms(r)): the parity tests' element-wise
+    relative error."""
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r)))
+    return float(np.max(np.abs(a - r) / np.maximum(np.abs(r), rms)))
 
 
-def cpu_baseline(w, g, n_tokens, gpu=None):
-    """The CPU oracle, untouched, on the first n_tokens tokens of the batch
-    (forward + backward).  Reported in the same unit (useful TFLOP/s).  With
-    `gpu` (the GPU step's y, dx and topk_idx of those tokens) it also reports
-    their agreement: routing (near-ties counted apart) and the max-norm
-    relative error ||g - r||_inf / ||r||_inf of y and dx on the tokens whose
-    routing agrees."""
+def cpu_baseline(w, g, gpu=None, budget_s=20.0, first_tokens=512):
+    """The CPU oracle, untouched, on the first n tokens of the batch (forward,
+    plus backward for the fwd+bwd workload), in the same unit (useful
+    TFLOP/s).  The inputs are handed over as fp32 arrays, converted before the
+    clock starts.  A first run on `first_tokens` tokens measures the host; n
+    is then chosen so that the reported run takes about `budget_s` seconds (at
+    most the whole batch).  With `gpu` (the GPU step's y, dx and topk_idx of
+    every token) it also reports their agreement on the timed tokens: routing
+    (near-ties counted apart) and the element-wise relative error of y and dx
+    on the tokens whose routing agrees."""
     import torch
     from oracle import moe_oracle as O
     from fine_grained_moe_amd.synthetic import useful_flops
     tn = lambda t: t.detach().float().cpu().numpy()
-    sub = dict(x=tn(g["x"][:n_tokens]), w_router=tn(g["w_router"]), bias=tn(g["bias"]),
-               w1=LazyExperts(g["w1"]), w2=LazyExperts(g["w2"]),
-               w1_sh=tn(g["w1_sh"]), w2_sh=tn(g["w2_sh"]))
-    backward = bool(w.backward) and "dy" in g   # the workload's own direction
-    dy = tn(g["dy"][:n_tokens]) if backward else None
-    threads = torch.get_num_threads()
-    t0 = time.perf_counter()
-    fwd = O.forward(sub, w.K, 128)
-    bwd = O.backward(sub, fwd, dy) if backward else None
-    dt = time.perf_counter() - t0
-    flops = useful_flops(w.with_(T=n_tokens), backward)
+    E = g["w1"].shape[0]
+    W1 = np.empty(tuple(g["w1"].shape), np.float32)
+    W2 = np.empty(tuple(g["w2"].shape), np.float32)
+    for e in range(E):
+        W1[e] = tn(g["w1"][e])
+        W2[e] = tn(g["w2"][e])
+    x_all, dy_all = tn(g["x"]), (tn(g["dy"]) if "dy" in g else None)
+    backward = bool(w.backward) and dy_all is not None   # the workload's own direction
+
+    def run(n):
+        sub = dict(x=x_all[:n], w_router=tn(g["w_router"]), bias=tn(g["bias"]), w1=W1, w2=W2,
+                   w1_sh=tn(g["w1_sh"]), w2_sh=tn(g["w2_sh"]))
+        t0 = time.perf_counter()
+        fwd = O.forward(sub, w.K, 128)
+        bwd = O.backward(sub, fwd, dy_all[:n]) if backward else None
+        return time.perf_counter() - t0, fwd, bwd
+
+    n0 = min(first_tokens, w.T)
+    dt, fwd, bwd = run(n0)
+    n = min(w.T, max(n0, int(n0 * budget_s / dt) // 64 * 64))
+    first = (n0, dt)
+    if n > n0:
+        del fwd, bwd
+        dt, fwd, bwd = run(n)
+    flops = useful_flops(w.with_(T=n), backward)
     cores = len(os.sched_getaffinity(0))
     cpu_model = ""
     try:
@@ -399,20 +421,19 @@ def cpu_baseline(w, g, n_tokens, gpu=None):
     res = dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, cpu_model=cpu_model,
                kind="oracle",
                sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
-                       f"first {n_tokens} of the {w.T} tokens at the same shapes, one run, "
-                       f"{dt:.1f} s; BLAS threads {threads}"),
-               seconds=dt)
+                       f"first {n} of the {w.T} tokens at the same shapes (all {E} experts' "
+                       f"weights), one run, {dt:.1f} s, after a {first[0]}-token run of "
+                       f"{first[1]:.1f} s that sized it; inputs converted to fp32 beforehand; "
+                       f"BLAS threads {torch.get_num_threads()}"),
+               seconds=dt, tokens=n)
     if gpu is not None:
         tie = np.asarray(fwd["route"]["near_tie"], bool)
-        same = np.all(gpu["topk_idx"] == fwd["route"]["topk_idx"], axis=1)
-
-        def err(a, r):
-            return float(np.max(np.abs(a - r)) / np.max(np.abs(r)))
-        par = {"tokens": int(len(same)), "near_ties": int(tie.sum()),
+        same = np.all(gpu["topk_idx"][:n] == fwd["route"]["topk_idx"], axis=1)
+        par = {"tokens": int(n), "near_ties": int(tie.sum()),
                "routing_differs_outside_near_ties": int((~same & ~tie).sum()),
-               "y_max_rel_err": err(gpu["y"][same], fwd["y"][same])}
+               "y_elementwise_rel_err": _elementwise_err(gpu["y"][:n][same], fwd["y"][same])}
         if backward:
-            par["dx_max_rel_err"] = err(gpu["dx"][same], bwd["dx"][same])
+            par["dx_elementwise_rel_err"] = _elementwise_err(gpu["dx"][:n][same], bwd["dx"][same])
         res["parity"] = par
     return res
 
@@ -520,6 +541,78 @@ def shard_cpu_baseline(g, R, F, w, n_experts):
                         f"(all {R} rows each), {dt:.1f} s; BLAS threads {torch.get_num_threads()}"))
 
 
+FORWARD_CONFIGS = ("decode", "prefill", "skew")
+
+
+def forward_config(M, name, steps, warmup):
+    """One forward configuration (its own seeded inputs): the whole forward
+    timed over `steps` steps (eager, and captured as one graph), every
+    grouped-GEMM launch and routing/permutation/combine call by its own
+    events, the dominant launch against its roofline."""
+    import torch
+    from fine_grained_moe_amd.synthetic import WORKLOADS, generate_torch, useful_flops
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    g = generate_torch(w, dev, with_dy=False)
+    layer = Layer(M, g, w.K)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+    names = Layer.GEMMS[:4]
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names + ROW_OPS_FWD} for _ in range(steps)]
+    for i in range(steps):
+        layer.forward(evs[i])
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(steps):
+        layer.forward()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms = f0.elapsed_time(f1) / steps
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        layer.forward()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward()
+    graph.replay()
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = f0.elapsed_time(f1) / steps
+    del graph
+    launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    row_us = {n: 1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs]))
+              for n in ROW_OPS_FWD}
+    live = int((layer.b["perm"]["counts"] > 0).sum().item())
+    dom = max(names, key=lambda n: launch_ms[n])
+    tf = useful_flops(w, False) / (ms * 1e-3) / 1e12
+    res = {"workload": (f"dots.llm1 MoE FFN layer forward, T={w.T}, H={w.H}, {w.E} routed experts "
+                        f"of width {w.F}, top-{w.K}, {w.S} shared experts"
+                        + (", Zipf(1.2) selection bias" if w.bias_kind == "zipf" else "")),
+           "T": w.T, "seed": w.seed, "ms": round(ms, 4), "tflops": round(tf, 2),
+           "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+           "graph_ms": round(graph_ms, 4), "routed_nonempty_experts": live,
+           "roofline": roofline_of(dom, w, launch_ms[dom], traffic=False, live=live),
+           "gemm_launches": {n: {"ms": round(launch_ms[n], 4),
+                                 "tflops": round(gemm_launch_flops(w, n) / (launch_ms[n] * 1e-3) / 1e12, 1),
+                                 "algorithmic_gb": round(gemm_launch_bytes(w, n, live) / 1e9, 3)}
+                             for n in names},
+           "row_ops_us": {n: round(row_us[n], 2) for n in ROW_OPS_FWD}}
+    del layer, g
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -556,7 +649,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; events inside bracket every grouped-GEMM launch
+    # eager steps with an event pair around every grouped-GEMM launch and
+    # every routing / permutation / combine call: each launch has the card to
+    # itself, so these time each kernel alone (the roofline entry's source)
     names = Layer.GEMMS if backward else Layer.GEMMS[:4]
     row_names = ROW_OPS_FWD + (ROW_OPS_BWD if backward else ())
     evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -564,23 +659,18 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_start.record(stream)
     for i in range(args.steps):
-        if i:
-            marks[i - 1].record(stream)
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    bounds = [t_start] + marks[:args.steps - 1] + [t_end]
-    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+    eager_ms = t_start.elapsed_time(t_end) / args.steps
     launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
     gemm_ms = sum(launch_ms.values())
     row_us = {n: 1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs]))
               for n in row_names}
 
-    # forward alone, timed the same way
+    # forward alone, eager, timed the same way
     torch.cuda.synchronize()
     f0 = torch.cuda.Event(enable_timing=True)
     f1 = torch.cuda.Event(enable_timing=True)
@@ -591,11 +681,29 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
 
-    # the same step captured once as a HIP graph and replayed (every entry
-    # point only launches kernels on the stream, into preallocated buffers);
-    # context beside the eager time, which stays the metric because the
-    # per-launch events need eager launches
-    graph_ms = graph2_ms = None
+    def timed_replays(graph):
+        """W untimed replays, then exactly K timed ones between two events,
+        synchronised on both sides, with an event at every step boundary."""
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        marks[0].record(stream)
+        for i in range(args.steps):
+            graph.replay()
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+        return marks[0].elapsed_time(marks[-1]) / args.steps, per
+
+    # the step as the layer runs it: captured once as a HIP graph with the
+    # independent launches on a second stream (the shared experts' products
+    # beside the router, permute and routed forward; the shared data
+    # gradients and every weight gradient beside the routed data gradients),
+    # results bit-identical to the eager step.  Its replays are the timed
+    # region of the metric; the one-stream graph is timed beside it.
+    graph_ms = None
+    ms, step_ms, schedule = eager_ms, None, "eager, one stream"
     if not args.no_graph:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -606,33 +714,19 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
-        graph.replay()
-        torch.cuda.synchronize()
-        r0 = torch.cuda.Event(enable_timing=True)
-        r1 = torch.cuda.Event(enable_timing=True)
-        r0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        r1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = r0.elapsed_time(r1) / args.steps
+        graph_ms, _ = timed_replays(graph)
         del graph
-        # the two-stream schedule of the same step, captured the same way
         side2 = torch.cuda.Stream()
         layer.step_two_streams(side2, backward)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             layer.step_two_streams(side2, backward)
-        graph.replay()
-        torch.cuda.synchronize()
-        r0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        r1.record(stream)
-        torch.cuda.synchronize()
-        graph2_ms = r0.elapsed_time(r1) / args.steps
+        ms, step_ms = timed_replays(graph)
+        schedule = "HIP graph, two streams"
         del graph
+    else:
+        step_ms = [ms] * args.steps
 
     # the step with load balancing (balance loss forward/backward, its dense
     # router gradients, the bias step), and each of those launches
@@ -662,7 +756,7 @@ def main():
         part_tf = dense_flops / 2 * (6 + 3) / (op_us["route_bwd_dense"] * 1e-6) / 1e12
         bal = {"seq_len": SEQ_LEN, "alpha": ALPHA, "gamma": GAMMA,
                "ms_per_step": round(bal_ms, 4),
-               "extra_ms": round(bal_ms - ms, 4),
+               "extra_ms": round(bal_ms - eager_ms, 4),   # both eager
                **{f"{n}_us": round(op_us[n], 2) for n in BALANCE_OPS},
                "route_bwd_dense_roofline": {"bound": "mfma", "achieved": round(part_tf, 2),
                                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -691,6 +785,8 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "ms_per_step_min": round(float(np.min(step_ms)), 4),
+        "schedule": schedule,
+        "eager_ms_per_step": round(eager_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -706,8 +802,7 @@ def main():
         "fwd_pct_of_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "gemm_pct_of_bf16_peak": round(100 * gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "gemm_ms": round(gemm_ms, 4),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
-        "graph_two_streams_ms_per_step": None if graph2_ms is None else round(graph2_ms, 4),
+        "graph_one_stream_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "routed_nonempty_experts": live,
         "roofline": roofline_of(dom, w, launch_ms[dom], live=live),
         "gemm_launches": launches,
@@ -722,18 +817,26 @@ def main():
     }
     if bal is not None:
         out["load_balancing"] = bal
+    gpu_out = None
     if not args.no_cpu_baseline:
         # the plain step once more, so that y and dx hold its outputs (the
         # balance loop changed dx); a token's y and dx depend on that token
         # only, so the oracle's run on the first tokens checks them
         step()
         torch.cuda.synchronize()
-        n = min(args.cpu_tokens, w.T)
-        gpu = {"y": layer.b["y"][:n].float().cpu().numpy(),
-               "topk_idx": layer.b["topk_idx"][:n].cpu().numpy()}
+        gpu_out = {"y": layer.b["y"].float().cpu().numpy(),
+                   "topk_idx": layer.b["topk_idx"].cpu().numpy()}
         if backward:
-            gpu["dx"] = layer.b["dx"][:n].float().cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_tokens, gpu)
+            gpu_out["dx"] = layer.b["dx"].float().cpu().numpy()
+    if backward and not args.no_configs:
+        # the other configurations of the layer, forward only, each on its own
+        # seeded inputs (the step's buffers freed first)
+        del layer
+        torch.cuda.empty_cache()
+        out["configs"] = {n: forward_config(M, n, max(args.steps // 2, 5), 3)
+                          for n in FORWARD_CONFIGS}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, g, gpu_out, budget_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

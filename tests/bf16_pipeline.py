@@ -87,14 +87,16 @@ def fuse_shared(w1_sh, w2_sh):
     return w1, w2
 
 
-def layer(inp, K, align, dy=None, rnd=bf16_store, route=None):
+def layer(inp, K, align, dy=None, rnd=bf16_store, route=None, router_extra=None):
     """Forward (and backward when dy is given) of the layer with bf16 stores.
 
     Routing is the oracle's fp32 routing unless `route` (a dict with
     topk_idx, topk_w, topk_s, as the oracle's route returns) is given: the
     HIP path's own routing, so that a near-tie token does not move segments.
-    Returns a dict of the stored tensors (fp64 arrays holding bf16 or fp32
-    values)."""
+    router_extra = (dW_r, dx_r): router gradients of another loss (the
+    sequence-wise balance loss), added to the combine path's in fp32 before
+    dx is summed and stored.  Returns a dict of the stored tensors (fp64
+    arrays holding bf16 or fp32 values)."""
     x = np.asarray(inp["x"], F64)
     T, H = x.shape
     E = inp["w1"].shape[0]
@@ -162,6 +164,9 @@ def layer(inp, K, align, dy=None, rnd=bf16_store, route=None):
                    dW2_sh=np.stack([dW2f[:, s * F:(s + 1) * F] for s in range(S)]))
         dx = dx + dx_sh
     dW_r, dx_r, _ = O.router_bwd(inp["x"], inp["w_router"], idx, r["topk_s"], dg)
+    if router_extra is not None:
+        dW_r = dW_r + router_extra[0]
+        dx_r = dx_r + router_extra[1]
     dW_r = dW_r.astype(np.float32).astype(F64)
     dx_r = dx_r.astype(np.float32).astype(F64)
     out.update(dW_r=dW_r, dx_router=dx_r, dx=rnd(dx + dx_r))

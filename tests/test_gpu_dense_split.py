@@ -35,8 +35,7 @@ CASES = {
 def _report():
     P.REPORT.clear()
     yield
-    for name, e, n, el in P.REPORT:
-        print(f"  {name:30s} max {e:.2e}  norm {n:.2e}  elementwise {el:.2e}", flush=True)
+    P.print_report()
 
 
 @pytest.mark.parametrize("name", sorted(CASES))

@@ -41,9 +41,7 @@ def _report():
     own element-wise error and the kernels' error against it."""
     P.REPORT.clear()
     yield
-    for name, e, n, e_emu, e_kern in P.REPORT:
-        extra = "" if e_emu is None else f"  storage {e_emu:.2e}  kernel {e_kern:.2e}"
-        print(f"  {name:40s} elementwise {e:.2e}  norm {n:.2e}{extra}", flush=True)
+    P.print_report()
 
 
 class LazyExperts:
@@ -147,15 +145,26 @@ def full_layer_checks(M, inp, K, backward=True, label=""):
                    emu["dact"][:nv][ev])
     P.assert_close(f"{label} dx_rows", P.to_np(grads["dx_rows"])[valid], dx_rows_ref[valid],
                    emu["dx_rows"][:nv][ev])
-    P.per_slice_close(f"{label} dW1", P.to_np(grads["dw1"]), dW1_ref, emu["dW1"])
-    P.per_slice_close(f"{label} dW2", P.to_np(grads["dw2"]), dW2_ref, emu["dW2"])
+    # sums of absolute products of each expert's stored factors (the scale of
+    # the componentwise gate), from the pipeline's stores on the same rows
+    eo, ec = emu["perm"]["offsets"], emu["perm"]["counts"]
+
+    def abs_prod(a, b):
+        return lambda e: np.abs(a[eo[e]:eo[e] + ec[e]]).T @ np.abs(b[eo[e]:eo[e] + ec[e]])
+    sc_dw1 = abs_prod(emu["dact"], emu["x_rows"])
+    sc_dw2 = abs_prod(emu["dy_rows"], emu["h"])
+    P.per_slice_close(f"{label} dW1", P.to_np(grads["dw1"]), dW1_ref, emu["dW1"], sc_dw1)
+    P.per_slice_close(f"{label} dW2", P.to_np(grads["dw2"]), dW2_ref, emu["dW2"], sc_dw2)
     if S > 0:
         dW1s, dW2s = unfuse_shared(P.to_np(grads["dw1_sh"])[0], P.to_np(grads["dw2_sh"])[0], S)
+        x64 = np.asarray(inp["x"], np.float64)
+        s1, s2 = unfuse_shared(np.abs(emu["dact_sh"]).T @ np.abs(x64),
+                               np.abs(np.asarray(dy, np.float64)).T @ np.abs(emu["h_sh"]), S)
         for s in range(S):
             a, _, _ = O.expert_ffn(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s])
             _, dw1r, dw2r, _ = O.expert_ffn_bwd(inp["x"], inp["w1_sh"][s], inp["w2_sh"][s], a, dy)
-            P.assert_close(f"{label} dW1_sh[{s}]", dW1s[s], dw1r, emu["dW1_sh"][s])
-            P.assert_close(f"{label} dW2_sh[{s}]", dW2s[s], dw2r, emu["dW2_sh"][s])
+            P.assert_close(f"{label} dW1_sh[{s}]", dW1s[s], dw1r, emu["dW1_sh"][s], s1[s])
+            P.assert_close(f"{label} dW2_sh[{s}]", dW2s[s], dw2r, emu["dW2_sh"][s], s2[s])
     # router backward, on the GPU's own routing and dg (fp32 sums of fp32 inputs)
     dWr_ref, dxr_ref, _ = O.router_bwd(inp["x"], inp["w_router"], idx, P.to_np(ctx["topk_s"]),
                                         P.to_np(grads["dg"]))
@@ -171,8 +180,10 @@ def full_layer_checks(M, inp, K, backward=True, label=""):
     ref_bwd = O.backward(inp, ref_fwd, dy)
     P.assert_close(f"{label} dx", P.to_np(grads["dx"])[same], ref_bwd["dx"][same])
     if same.all():
-        P.per_slice_close(f"{label} dW1 (e2e)", P.to_np(grads["dw1"]), ref_bwd["dW1"], emu["dW1"])
-        P.per_slice_close(f"{label} dW2 (e2e)", P.to_np(grads["dw2"]), ref_bwd["dW2"], emu["dW2"])
+        P.per_slice_close(f"{label} dW1 (e2e)", P.to_np(grads["dw1"]), ref_bwd["dW1"], emu["dW1"],
+                          sc_dw1)
+        P.per_slice_close(f"{label} dW2 (e2e)", P.to_np(grads["dw2"]), ref_bwd["dW2"], emu["dW2"],
+                          sc_dw2)
         P.assert_close(f"{label} dW_r (e2e)", P.to_np(grads["dw_router"]), ref_bwd["dW_r"],
                        emu["dW_r"])
     return dict(n_diff=n_diff, n_tie=n_tie)
@@ -401,10 +412,12 @@ def unit_wgrad_checks(name, x_all, dy_all, w1e, w2e, dw1, dw2, units):
         au, _, _ = O.expert_ffn(x_all, w1u, w2u)
         _, dw1u, dw2u, _ = O.expert_ffn_bwd(x_all, w1u, w2u, au, dy_all)
         ae, he, _ = B.expert_forward(x_all, w1u, w2u)
-        _, dw1e, dw2e, _ = B.expert_backward(x_all, w1u, w2u, ae, he, dy_all)
-        P.assert_close(f"{name} dW1[{f}] gate", P.to_np(dw1[f]), dw1u[0], dw1e[0])
-        P.assert_close(f"{name} dW1[{F + f}] up", P.to_np(dw1[F + f]), dw1u[1], dw1e[1])
-        P.assert_close(f"{name} dW2[:,{f}]", P.to_np(dw2[:, f]), dw2u[:, 0], dw2e[:, 0])
+        _, dw1e, dw2e, dae = B.expert_backward(x_all, w1u, w2u, ae, he, dy_all)
+        s1 = np.abs(dae).T @ np.abs(np.asarray(x_all, np.float64))   # [2, H]
+        s2 = np.abs(np.asarray(dy_all, np.float64)).T @ np.abs(he)   # [H, 1]
+        P.assert_close(f"{name} dW1[{f}] gate", P.to_np(dw1[f]), dw1u[0], dw1e[0], s1[0])
+        P.assert_close(f"{name} dW1[{F + f}] up", P.to_np(dw1[F + f]), dw1u[1], dw1e[1], s1[1])
+        P.assert_close(f"{name} dW2[:,{f}]", P.to_np(dw2[:, f]), dw2u[:, 0], dw2e[:, 0], s2[:, 0])
 
 
 def sampled_checks(M, w, backward, n_tokens=12, n_experts=4, n_units=3, seed=0):
@@ -497,12 +510,16 @@ def sampled_checks(M, w, backward, n_tokens=12, n_experts=4, n_units=3, seed=0):
             au, _, _ = O.expert_ffn(x, w1u, w2u)
             _, dw1u, dw2u, _ = O.expert_ffn_bwd(x, w1u, w2u, au, dy)
             ae, he, _ = B.expert_forward(x, w1u, w2u)
-            _, dw1e, dw2e, _ = B.expert_backward(x, w1u, w2u, ae, he, dy)
+            _, dw1e, dw2e, dae = B.expert_backward(x, w1u, w2u, ae, he, dy)
+            s1 = np.abs(dae).T @ np.abs(np.asarray(x, np.float64))
+            s2 = np.abs(np.asarray(dy, np.float64)).T @ np.abs(he)
             gate_row, up_row = s * F + f, S * F + s * F + f
-            P.assert_close(f"{w.name} dW1_sh[{s},{f}] gate", P.to_np(dw1f[gate_row]), dw1u[0], dw1e[0])
-            P.assert_close(f"{w.name} dW1_sh[{s},{f}] up", P.to_np(dw1f[up_row]), dw1u[1], dw1e[1])
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] gate", P.to_np(dw1f[gate_row]), dw1u[0],
+                           dw1e[0], s1[0])
+            P.assert_close(f"{w.name} dW1_sh[{s},{f}] up", P.to_np(dw1f[up_row]), dw1u[1], dw1e[1],
+                           s1[1])
             P.assert_close(f"{w.name} dW2_sh[{s},{f}]", P.to_np(dw2f[:, s * F + f]), dw2u[:, 0],
-                           dw2e[:, 0])
+                           dw2e[:, 0], s2[:, 0])
 
     # router gradient, full, on the GPU's own routing and dg
     dWr_ref, _, _ = O.router_bwd(x, wr, idx, P.to_np(ctx["topk_s"]), P.to_np(grads["dg"]))
