@@ -162,8 +162,31 @@ moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t ali
   REQUIRE_ALIGNED(topk_idx, x, counts, offsets, row_of, src_token, tile_expert, x_rows);
   REQUIRE_WS_ALIGNED(ws);
   return hip_status(moe::launch_permute(T, H, E, K, align, topk_idx, x, m_cap, counts, offsets,
-                                        row_of, src_token, tile_expert, x_rows, ws,
+                                        row_of, src_token, tile_expert, x_rows, ws, nullptr,
                                         (hipStream_t)stream),
+                    __func__);
+}
+
+int32_t moe_permute_noalloc_max_tokens(void) { return moe::permute_noalloc_max_tokens(); }
+
+moe_status_t moe_permute_noalloc(int32_t T, int32_t H, int32_t E, int32_t K, int32_t align,
+                                 const int32_t* topk_idx, const uint16_t* x, int64_t m_cap,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                 int32_t* src_token, int32_t* tile_expert, uint16_t* x_rows,
+                                 int32_t* status, void* stream) {
+  moe_status_t st = check_dims(__func__, T, H, E, K);
+  if (st) return st;
+  REQUIRE(T <= moe::permute_noalloc_max_tokens(), MOE_ERR_UNSUPPORTED_SHAPE,
+          "T > moe_permute_noalloc_max_tokens() (the size of its static scratch)");
+  REQUIRE(align == moe::kAlign, MOE_ERR_UNSUPPORTED_SHAPE, "align != moe_align()");
+  REQUIRE(m_cap >= capacity(T, E, K) && m_cap % align == 0 && m_cap < ((int64_t)1 << 31),
+          MOE_ERR_INVALID_ARGUMENT, "m_cap below moe_capacity_rows or not a multiple of align");
+  REQUIRE(counts && offsets && src_token && tile_expert, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(T == 0 || (topk_idx && x && row_of && x_rows), MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE_ALIGNED(topk_idx, x, counts, offsets, row_of, src_token, tile_expert, x_rows, status);
+  return hip_status(moe::launch_permute_noalloc(T, H, E, K, align, topk_idx, x, m_cap, counts,
+                                                offsets, row_of, src_token, tile_expert, x_rows,
+                                                status, (hipStream_t)stream),
                     __func__);
 }
 

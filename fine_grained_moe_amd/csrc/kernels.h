@@ -22,7 +22,14 @@ size_t permute_workspace_bytes(int T, int E);
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
                           const uint16_t* x, int64_t m_cap, int32_t* counts, int32_t* offsets,
                           int32_t* row_of, int32_t* src_token, int32_t* tile_expert,
-                          uint16_t* x_rows, void* ws, hipStream_t s);
+                          uint16_t* x_rows, void* ws, int32_t* status_out, hipStream_t s);
+// the same without a workspace: the kernels use a file-scope device array
+int permute_noalloc_max_tokens();
+hipError_t launch_permute_noalloc(int T, int H, int E, int K, int align, const int32_t* topk_idx,
+                                  const uint16_t* x, int64_t m_cap, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                                  int32_t* tile_expert, uint16_t* x_rows, int32_t* status,
+                                  hipStream_t s);
 
 hipError_t launch_gemm_gate_up(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
                                const int32_t* counts, const int32_t* tile_expert,

@@ -22,6 +22,9 @@
 //   [1] number of rejected tokens
 //   [2] smallest rejected token, -1 if none
 //   [3] kPermuteStatusMagic
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -241,9 +244,9 @@ size_t permute_workspace_bytes(int T, int E) {
 hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* topk_idx,
                           const uint16_t* x, int64_t m_cap, int32_t* counts, int32_t* offsets,
                           int32_t* row_of, int32_t* src_token, int32_t* tile_expert,
-                          uint16_t* x_rows, void* ws, hipStream_t s) {
+                          uint16_t* x_rows, void* ws, int32_t* status_out, hipStream_t s) {
   const int nchunks = (T + perm::CH - 1) / perm::CH;
-  int32_t* status = (int32_t*)ws;
+  int32_t* status = status_out ? status_out : (int32_t*)ws;
   int32_t* chunk_status = (int32_t*)((uint8_t*)ws + kPermuteStatusBytes);
   int32_t* chunk_counts = (int32_t*)((uint8_t*)chunk_status + chunk_status_bytes(nchunks));
   int32_t* chunk_base = chunk_counts + (size_t)nchunks * E;
@@ -262,6 +265,70 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
                        x_rows);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The permutation without a workspace argument, for callers that cannot
+// allocate (graph capture, serving loops): its workspace is this file-scope
+// device array, one per GPU for the life of the process.  Every word the
+// kernels read is written earlier in the same call, so nothing is cleared
+// between calls; calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+namespace perm {
+constexpr int kNoAllocMaxTokens = 131072;
+constexpr size_t kNoAllocScratchBytes =
+    kPermuteStatusBytes + ((size_t)3 * (kNoAllocMaxTokens / CH) * 4 + 255) / 256 * 256 +
+    (size_t)2 * (kNoAllocMaxTokens / CH) * EMAX * 4;   // 530,688 bytes
+static_assert(kNoAllocMaxTokens % CH == 0, "whole chunks");
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+}  // namespace perm
+
+namespace {
+using perm::kNoAllocMaxTokens;
+using perm::kNoAllocScratchBytes;
+
+// the array's device address on each GPU, looked up once per device (in host
+// code `scratch` names a host-side stand-in, never the device memory)
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(perm::scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+int permute_noalloc_max_tokens() { return kNoAllocMaxTokens; }
+
+hipError_t launch_permute_noalloc(int T, int H, int E, int K, int align, const int32_t* topk_idx,
+                                  const uint16_t* x, int64_t m_cap, int32_t* counts,
+                                  int32_t* offsets, int32_t* row_of, int32_t* src_token,
+                                  int32_t* tile_expert, uint16_t* x_rows, int32_t* status,
+                                  hipStream_t s) {
+  if (T > kNoAllocMaxTokens || E > perm::EMAX ||
+      permute_workspace_bytes(T, E) > kNoAllocScratchBytes)
+    return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_permute(T, H, E, K, align, topk_idx, x, m_cap, counts, offsets, row_of, src_token,
+                        tile_expert, x_rows, ws, status, s);
 }
 
 }  // namespace moe

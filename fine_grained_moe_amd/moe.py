@@ -30,6 +30,9 @@ _SIGS = {
     "moe_route_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_permute_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_permute_check": (_i32, [_p]),
+    "moe_permute_noalloc_max_tokens": (_i32, []),
+    "moe_permute_noalloc": (_i32, [_i32, _i32, _i32, _i32, _i32, _p, _p, _i64, _p, _p, _p, _p, _p,
+                                   _p, _p, _p]),
     "moe_route_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_seq_balance_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_bwd_dense_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -198,6 +201,32 @@ def moe_permute(topk_idx, x, E, m_cap=None, out=None, ws=None):
                             _ptr(out["tile_expert"], I32), _ptr(out["x_rows"], BF16),
                             _ptr(ws), ws.numel(), _stream()))
     out["status"] = ws[:16].view(I32)
+    return out
+
+
+def moe_permute_noalloc_max_tokens() -> int:
+    return int(_lib.moe_permute_noalloc_max_tokens())
+
+
+def moe_permute_noalloc(topk_idx, x, E, out, status=None):
+    """moe_permute without a workspace (the library's static device array):
+    every output buffer comes from the caller in `out` (the dict moe_permute
+    returns, x_rows included), so the call allocates nothing.  status: int32
+    [4] device tensor receiving the data-check block, or None.  Returns out."""
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    A = moe_align()
+    m_cap = out["src_token"].shape[0]
+    _expect(x=(x, (T, H)), counts=(out["counts"], (E,)), offsets=(out["offsets"], (E + 1,)),
+            row_of=(out["row_of"], (T, K)), src_token=(out["src_token"], (m_cap,)),
+            tile_expert=(out["tile_expert"], (m_cap // A,)), x_rows=(out["x_rows"], (m_cap, H)),
+            status=(status, (4,)))
+    _check(_lib.moe_permute_noalloc(T, H, E, K, A, _ptr(topk_idx, I32, "topk_idx"),
+                                    _ptr(x, BF16, "x"), m_cap, _ptr(out["counts"], I32),
+                                    _ptr(out["offsets"], I32), _ptr(out["row_of"], I32),
+                                    _ptr(out["src_token"], I32), _ptr(out["tile_expert"], I32),
+                                    _ptr(out["x_rows"], BF16), _ptr(status, I32, "status"),
+                                    _stream()))
     return out
 
 

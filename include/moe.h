@@ -163,6 +163,28 @@ moe_status_t moe_permute(int32_t T, int32_t H, int32_t E, int32_t K, int32_t ali
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc - moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same permutation and data check, same arguments
+ * and results, but no workspace argument.  Its kernels use a static device
+ * array of the library (530,688 bytes on each GPU it runs on, held until the
+ * process ends), which bounds T to moe_permute_noalloc_max_tokens() (131,072);
+ * larger T is rejected with MOE_ERR_UNSUPPORTED_SHAPE.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).  Every word of the
+ * array the kernels read is written earlier in the same call, so nothing
+ * carries over from the previous call; calls that overlap in time on one GPU
+ * share the array and race (serialise them, e.g. on one stream).
+ * status: device int32 [4] (nullable) that receives the data-check block
+ * (see moe_permute / moe_permute_check); with NULL it stays in the array.
+ */
+int32_t moe_permute_noalloc_max_tokens(void);
+moe_status_t moe_permute_noalloc(int32_t T, int32_t H, int32_t E, int32_t K, int32_t align,
+                                 const int32_t* topk_idx, const uint16_t* x, int64_t m_cap,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                 int32_t* src_token, int32_t* tile_expert, uint16_t* x_rows,
+                                 int32_t* status, void* stream);
+
+/*
  * moe_permute_check - host: decodes moe_permute's data-check block.
  * words: host copy of the first four int32 of moe_permute's workspace.
  * Returns MOE_OK when no token was rejected; MOE_ERR_INVALID_ARGUMENT when
