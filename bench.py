@@ -403,13 +403,24 @@ def cpu_baseline(w, g, gpu=None, budget_s=20.0, first_tokens=512):
         bwd = O.backward(sub, fwd, dy_all[:n]) if backward else None
         return time.perf_counter() - t0, fwd, bwd
 
+    # two sizing runs: the oracle's time is a fixed part (it converts every
+    # expert's weights to fp64 once per pass) plus a part per token
     n0 = min(first_tokens, w.T)
-    dt, fwd, bwd = run(n0)
-    n = min(w.T, max(n0, int(n0 * budget_s / dt) // 64 * 64))
-    first = (n0, dt)
-    if n > n0:
+    t0, fwd, bwd = run(n0)
+    n, dt, first = n0, t0, [(n0, t0)]
+    if w.T > n0:
         del fwd, bwd
-        dt, fwd, bwd = run(n)
+        n1 = min(w.T, 2 * n0)
+        t1, fwd, bwd = run(n1)
+        first.append((n1, t1))
+        per_token = max((t1 - t0) / (n1 - n0), 1e-9)
+        fixed = max(t0 - n0 * per_token, 0.0)
+        n, dt = n1, t1
+        target = min(w.T, max(n1, int((budget_s - fixed) / per_token) // 64 * 64))
+        if target > n1:
+            del fwd, bwd
+            n = target
+            dt, fwd, bwd = run(n)
     flops = useful_flops(w.with_(T=n), backward)
     cores = len(os.sched_getaffinity(0))
     cpu_model = ""
@@ -422,8 +433,9 @@ def cpu_baseline(w, g, gpu=None, budget_s=20.0, first_tokens=512):
                kind="oracle",
                sample=(f"fp64 NumPy oracle, {'forward+backward' if backward else 'forward'} of the "
                        f"first {n} of the {w.T} tokens at the same shapes (all {E} experts' "
-                       f"weights), one run, {dt:.1f} s, after a {first[0]}-token run of "
-                       f"{first[1]:.1f} s that sized it; inputs converted to fp32 beforehand; "
+                       f"weights), one run, {dt:.1f} s, sized by runs of "
+                       + ", ".join(f"{a} tokens ({b:.1f} s)" for a, b in first if a != n)
+                       + f"; inputs converted to fp32 beforehand; "
                        f"BLAS threads {torch.get_num_threads()}"),
                seconds=dt, tokens=n)
     if gpu is not None:
@@ -590,18 +602,37 @@ def forward_config(M, name, steps, warmup):
     torch.cuda.synchronize()
     graph_ms = f0.elapsed_time(f1) / steps
     del graph
+    # the forward as the layer runs it: one graph, the shared experts'
+    # products on a second stream beside the routing and routed products
+    side2 = torch.cuda.Stream()
+    layer.step_two_streams(side2, backward=False)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step_two_streams(side2, backward=False)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms2 = f0.elapsed_time(f1) / steps
+    del graph
     launch_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
     row_us = {n: 1e3 * float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs]))
               for n in ROW_OPS_FWD}
     live = int((layer.b["perm"]["counts"] > 0).sum().item())
     dom = max(names, key=lambda n: launch_ms[n])
-    tf = useful_flops(w, False) / (ms * 1e-3) / 1e12
+    tf = useful_flops(w, False) / (ms2 * 1e-3) / 1e12
     res = {"workload": (f"dots.llm1 MoE FFN layer forward, T={w.T}, H={w.H}, {w.E} routed experts "
                         f"of width {w.F}, top-{w.K}, {w.S} shared experts"
                         + (", Zipf(1.2) selection bias" if w.bias_kind == "zipf" else "")),
-           "T": w.T, "seed": w.seed, "ms": round(ms, 4), "tflops": round(tf, 2),
+           "T": w.T, "seed": w.seed, "ms": round(ms2, 4), "tflops": round(tf, 2),
            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
-           "graph_ms": round(graph_ms, 4), "routed_nonempty_experts": live,
+           "schedule": "HIP graph, two streams", "eager_ms": round(ms, 4),
+           "graph_one_stream_ms": round(graph_ms, 4), "routed_nonempty_experts": live,
            "roofline": roofline_of(dom, w, launch_ms[dom], traffic=False, live=live),
            "gemm_launches": {n: {"ms": round(launch_ms[n], 4),
                                  "tflops": round(gemm_launch_flops(w, n) / (launch_ms[n] * 1e-3) / 1e12, 1),
