@@ -93,6 +93,14 @@ using CfgWgrad = CfgWide;
 static_assert(CfgRows::BM == kAlign, "row tile must equal the segment alignment");
 
 constexpr int GROUP_M = 4;  // m-tiles per rasterization group (dense row products)
+// Routed row products: the tiles of one expert run in bands of BAND_M m-tiles
+// (all n-tiles of a band, m-tile fastest, before the next band).  The
+// workgroups that run together on one XCD then share BAND_M row blocks of the
+// row operand and a few weight slices; an expert with thousands of rows
+// rastered m-fastest over its whole segment instead streams every row block
+// once per n-tile (the skewed batch's gate/up forward: 14 % faster with bands
+// of 4; balanced batches, at most 4 row tiles per expert, are unchanged).
+constexpr int BAND_M = 4;
 // K-grouped weight gradients: m-tiles per rasterization group inside one
 // expert, so a column slab of the second operand is reused by several m-tiles
 // while it is resident in L2
@@ -254,8 +262,14 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
       const int mstart = a.offsets[e] / BM;
       const int me = (a.offsets[e + 1] - a.offsets[e]) / BM;
       const int local = L - a.n_ntiles * mstart;
-      mt = mstart + local % me;
-      nt = local / me;
+      // bands of BAND_M m-tiles, each band's tiles m-fastest within it and
+      // the bands one after the other (a segment of at most BAND_M tiles is
+      // one band)
+      const int per_band = BAND_M * a.n_ntiles;
+      const int band = local / per_band, within = local % per_band;
+      const int bm = min(BAND_M, me - band * BAND_M);
+      mt = mstart + band * BAND_M + within % bm;
+      nt = within / bm;
     }
   }
 
