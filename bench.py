@@ -40,14 +40,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "93cad6ca9c38af1306bcd0abe959cbdd50d4157bbdb812dac749931001e2dca0"
+TRAFFIC_SOURCE_SHA256 = "70b10f934d4993bfb73aa02c736f14f13c428271fc8e858beb58a582e1368446"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3065899.0, 405504.0), "down_fwd": (1102603.0, 491521.0),
-    "shared_gate_up_fwd": (348246.0, 135203.0), "shared_down_fwd": (180294.0, 81946.0),
-    "down_dgrad": (1927229.0, 270336.0), "gate_up_dgrad": (2550180.0, 491521.0),
-    "down_wgrad": (321312.0, 1802303.0), "gate_up_wgrad": (847759.0, 3605022.0),
-    "shared_down_dgrad": (352381.0, 90115.0), "shared_gate_up_dgrad": (360522.0, 81921.0),
-    "shared_down_wgrad": (217163.0, 28161.0), "shared_gate_up_wgrad": (434252.0, 56321.0),
+    "gate_up_fwd": (3048512.1, 405504.1), "down_fwd": (1088823.2, 491541.3),
+    "shared_gate_up_fwd": (348246.7, 135202.4), "shared_down_fwd": (180295.2, 81937.6),
+    "down_dgrad": (1889009.6, 270336.3), "gate_up_dgrad": (2565813.0, 491521.8),
+    "down_wgrad": (322259.3, 1802310.5), "gate_up_wgrad": (846597.1, 3605101.3),
+    "shared_down_dgrad": (352424.2, 90118.6), "shared_gate_up_dgrad": (360523.3, 81921.0),
+    "shared_down_wgrad": (217238.5, 28160.5), "shared_gate_up_wgrad": (436486.5, 56320.0),
 }
 
 
