@@ -12,6 +12,8 @@
 //                tokens with the same expert (popcount of a per-expert token
 //                bitmask), so rows of a segment are in ascending token order
 //   4. rows    : copy each token's x row into its K segment rows (x read once)
+// A batch of at most one chunk (decode) runs steps 1-3 as one workgroup
+// (small_kernel): the same layout from one launch instead of four.
 //
 // Data check: a token whose K expert ids are not all in [0,E) and distinct is
 // rejected before any of its ids indexes anything: it is not counted, owns no
@@ -207,6 +209,104 @@ __global__ void __launch_bounds__(CH) scatter_kernel(int T, int E, int K,
   }
 }
 
+// Steps 1-3 for a batch of at most CH tokens, one token per thread: the
+// histogram and the per-expert token bitmasks in LDS, the padded scan, every
+// row no token fills set to -1 (each segment's padding and the rows past the
+// last segment: the token rows are written by the scatter, so no row is
+// written twice), the tile -> expert table, and each token's rows in
+// ascending token order, as the multi-chunk path lays them out.
+__global__ void __launch_bounds__(CH) small_kernel(int T, int E, int K, int align, int64_t m_cap,
+                                                   const int32_t* __restrict__ topk_idx,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ row_of,
+                                                   int32_t* __restrict__ src_token,
+                                                   int32_t* __restrict__ tile_expert,
+                                                   int32_t* __restrict__ status) {
+  __shared__ int hist[EMAX];
+  __shared__ int scan[2][EMAX];
+  __shared__ int off[EMAX + 1];
+  __shared__ uint32_t mask[EMAX][CH / 32];
+  __shared__ int bad_flags, bad_count, bad_first;
+  const int tid = threadIdx.x;
+  if (tid < EMAX) hist[tid] = 0;
+  for (int i = tid; i < EMAX * (CH / 32); i += CH) (&mask[0][0])[i] = 0u;
+  if (tid == 0) {
+    bad_flags = 0;
+    bad_count = 0;
+    bad_first = kNone;
+  }
+  __syncthreads();
+  const int t = tid, w = tid >> 5, bit = tid & 31;
+  int ev[16];
+  bool ok = false;
+  if (t < T) {
+    const int fl = load_ids(topk_idx + (int64_t)t * K, K, E, ev);
+    ok = fl == 0;
+    if (ok) {
+      for (int k = 0; k < K; ++k) {
+        atomicAdd(&hist[ev[k]], 1);
+        atomicOr(&mask[ev[k]][w], 1u << bit);
+      }
+    } else {
+      atomicOr(&bad_flags, fl);
+      atomicAdd(&bad_count, 1);
+      atomicMin(&bad_first, t);
+      for (int k = 0; k < K; ++k) row_of[(int64_t)t * K + k] = -1;   // rejected: no rows
+    }
+  }
+  __syncthreads();
+  // inclusive scan of the padded counts over experts (Hillis-Steele, in LDS)
+  int cur = 0;
+  if (tid < EMAX) scan[0][tid] = tid < E ? (hist[tid] + align - 1) / align * align : 0;
+  __syncthreads();
+  for (int d = 1; d < EMAX; d <<= 1) {
+    if (tid < EMAX) scan[cur ^ 1][tid] = scan[cur][tid] + (tid >= d ? scan[cur][tid - d] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (tid <= E) off[tid] = tid == 0 ? 0 : scan[cur][tid - 1];
+  __syncthreads();
+  if (tid < E) counts[tid] = hist[tid];
+  if (tid <= E) offsets[tid] = off[tid];
+  if (tid == 0) {
+    status[0] = bad_flags;
+    status[1] = bad_count;
+    status[2] = bad_count ? bad_first : -1;
+    status[3] = kPermuteStatusMagic;
+  }
+  // rows no token fills: each segment's padding ...
+  for (int e = 0; e < E; ++e)
+    for (int r = off[e] + hist[e] + tid; r < off[e + 1]; r += CH) src_token[r] = -1;
+  // ... and every row past the last segment
+  for (int64_t r = off[E] + tid; r < m_cap; r += CH) src_token[r] = -1;
+  // tile -> expert: the last expert whose segment starts at or before the
+  // tile (a non-empty one), -1 past the last segment
+  for (int64_t q = tid; q * align < m_cap; q += CH) {
+    const int row = (int)(q * align);
+    int e = -1;
+    if (row < off[E]) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= row) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    tile_expert[q] = e;
+  }
+  if (ok) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ev[k];
+      int rank = __popc(mask[e][w] & ((1u << bit) - 1u));
+      for (int q = 0; q < w; ++q) rank += __popc(mask[e][q]);
+      const int row = off[e] + rank;
+      row_of[(int64_t)t * K + k] = row;
+      src_token[row] = t;
+    }
+  }
+}
+
 // one wave per token; each lane moves 16-byte chunks of the row
 __global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K,
                                                    const int32_t* __restrict__ row_of,
@@ -247,6 +347,13 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
                           uint16_t* x_rows, void* ws, int32_t* status_out, hipStream_t s) {
   const int nchunks = (T + perm::CH - 1) / perm::CH;
   int32_t* status = status_out ? status_out : (int32_t*)ws;
+  if (nchunks == 1) {
+    hipLaunchKernelGGL(perm::small_kernel, dim3(1), dim3(perm::CH), 0, s, T, E, K, align, m_cap,
+                       topk_idx, counts, offsets, row_of, src_token, tile_expert, status);
+    hipLaunchKernelGGL(perm::rows_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, H, K, row_of, x,
+                       x_rows);
+    return hipGetLastError();
+  }
   int32_t* chunk_status = (int32_t*)((uint8_t*)ws + kPermuteStatusBytes);
   int32_t* chunk_counts = (int32_t*)((uint8_t*)chunk_status + chunk_status_bytes(nchunks));
   int32_t* chunk_base = chunk_counts + (size_t)nchunks * E;

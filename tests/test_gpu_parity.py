@@ -318,17 +318,20 @@ def test_empty_batch(M):
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
 
 
-def test_permute_rejects_bad_ids(M):
+@pytest.mark.parametrize("T", [700, 200])
+def test_permute_rejects_bad_ids(M, T):
     """The permutation's data check: tokens with an expert id outside [0,E)
     (too large, negative) or repeated within the token are rejected before
     any id indexes memory (no rows, row_of -1, x row not copied) and reported
     in the status block; every other token is permuted exactly as the oracle
     permutes the valid tokens alone.  A second call with valid ids on the same
-    workspace reports nothing."""
-    T, H, E, K = 700, 128, 16, 4
+    workspace reports nothing.  T = 200 is one chunk (the single-workgroup
+    path), T = 700 three."""
+    H, E, K = 128, 16, 4
     rng = np.random.default_rng(91)
     idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
-    bad = {5: (2, E), 6: (0, -1), 300: (1, 1 << 30), 301: (3, None), 699: (0, None)}
+    mid = T // 2
+    bad = {5: (2, E), 6: (0, -1), mid: (1, 1 << 30), mid + 1: (3, None), T - 1: (0, None)}
     for t, (k, v) in bad.items():
         idx[t, k] = idx[t, (k + 1) % K] if v is None else v   # None: repeat another id
     x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV).to(torch.bfloat16)
