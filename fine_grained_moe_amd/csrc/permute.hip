@@ -275,9 +275,20 @@ __global__ void __launch_bounds__(CH) small_kernel(int T, int E, int K, int alig
     status[2] = bad_count ? bad_first : -1;
     status[3] = kPermuteStatusMagic;
   }
-  // rows no token fills: each segment's padding ...
-  for (int e = 0; e < E; ++e)
-    for (int r = off[e] + hist[e] + tid; r < off[e + 1]; r += CH) src_token[r] = -1;
+  // rows no token fills: each segment's padding, one wave per expert with its
+  // lanes on consecutive rows (coalesced stores); lane j of wave v first
+  // fetches the bounds of expert v + 4j, so the loop reads them from registers
+  {
+    constexpr int NWV = CH / 64;
+    const int wv = tid >> 6, ln = tid & 63;
+    const int ej = wv + NWV * ln;
+    const int pad_lo = ej < E ? off[ej] + hist[ej] : 0;
+    const int pad_hi = ej < E ? off[ej + 1] : 0;
+    for (int j = 0; wv + NWV * j < E; ++j) {
+      const int lo = __builtin_amdgcn_readlane(pad_lo, j), hi = __builtin_amdgcn_readlane(pad_hi, j);
+      for (int r = lo + ln; r < hi; r += 64) src_token[r] = -1;
+    }
+  }
   // ... and every row past the last segment
   for (int64_t r = off[E] + tid; r < m_cap; r += CH) src_token[r] = -1;
   // tile -> expert: the last expert whose segment starts at or before the
@@ -307,19 +318,21 @@ __global__ void __launch_bounds__(CH) small_kernel(int T, int E, int K, int alig
   }
 }
 
-// one wave per token; each lane moves 16-byte chunks of the row
-__global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K,
+// `split` waves per token (1, 2 or 4: small batches spread a row over
+// several waves to fill the chip); each lane moves 16-byte chunks of the row
+__global__ void __launch_bounds__(256) rows_kernel(int T, int H, int K, int split,
                                                    const int32_t* __restrict__ row_of,
                                                    const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ x_rows) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = gw / split, part = gw % split;
   if (t >= T || row_of[(int64_t)t * K] < 0) return;   // a rejected token owns no rows
   int rows[16];
   for (int k = 0; k < K; ++k) rows[k] = row_of[(int64_t)t * K + k];
   const int nchunk = H / 8;
   const u32x4* src = (const u32x4*)(x + (int64_t)t * H);
-  for (int c = lane; c < nchunk; c += 64) {
+  for (int c = part * 64 + lane; c < nchunk; c += 64 * split) {
     u32x4 v = src[c];
     // non-temporal: the K copies of a row do not displace the lines the next
     // products read (measured: this gather 4 %, the gate/up product after it
@@ -350,8 +363,8 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
   if (nchunks == 1) {
     hipLaunchKernelGGL(perm::small_kernel, dim3(1), dim3(perm::CH), 0, s, T, E, K, align, m_cap,
                        topk_idx, counts, offsets, row_of, src_token, tile_expert, status);
-    hipLaunchKernelGGL(perm::rows_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, H, K, row_of, x,
-                       x_rows);
+    // four waves a token: T <= 256 tokens as up to 1,024 waves
+    hipLaunchKernelGGL(perm::rows_kernel, dim3(T), dim3(256), 0, s, T, H, K, 4, row_of, x, x_rows);
     return hipGetLastError();
   }
   int32_t* chunk_status = (int32_t*)((uint8_t*)ws + kPermuteStatusBytes);
@@ -368,7 +381,7 @@ hipError_t launch_permute(int T, int H, int E, int K, int align, const int32_t* 
   if (nchunks > 0) {
     hipLaunchKernelGGL(perm::scatter_kernel, dim3(nchunks), dim3(perm::CH), 0, s, T, E, K,
                        topk_idx, chunk_base, offsets, row_of, src_token);
-    hipLaunchKernelGGL(perm::rows_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, H, K, row_of, x,
+    hipLaunchKernelGGL(perm::rows_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, H, K, 1, row_of, x,
                        x_rows);
   }
   return hipGetLastError();
