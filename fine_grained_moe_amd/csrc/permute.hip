@@ -18,8 +18,8 @@
 // Data check: a token whose K expert ids are not all in [0,E) and distinct is
 // rejected before any of its ids indexes anything: it is not counted, owns no
 // row, its row_of entries are -1 and its x row is not copied.  count records
-// per chunk what it rejected; scan folds that into the status block at the
-// start of the workspace (written by every call):
+// per chunk what it rejected; scan (or small_kernel, for one chunk) folds that
+// into the status block at the start of the workspace (written by every call):
 //   [0] flags: bit 0 an id outside [0,E), bit 1 an id repeated in a token
 //   [1] number of rejected tokens
 //   [2] smallest rejected token, -1 if none

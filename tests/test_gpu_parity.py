@@ -318,6 +318,38 @@ def test_empty_batch(M):
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
 
 
+@pytest.mark.parametrize("T,kind", [(1, "uniform"), (255, "uniform"), (256, "uniform"),
+                                    (257, "uniform"), (512, "uniform"), (256, "skewed"),
+                                    (257, "skewed")])
+def test_permute_chunk_boundary(M, T, kind):
+    """Batches on both sides of one 256-token chunk (the single-workgroup
+    layout below it, the multi-chunk kernels above) at E = 128, K = 6, every
+    output buffer pre-filled with a sentinel so that an unwritten entry shows:
+    the layout bit for bit against the oracle's, every x row copied.  skewed:
+    every token picks from the same eight experts, so segments run to T rows."""
+    H, E, K = 256, 128, 6
+    rng = np.random.default_rng(1000 + T)
+    pool = E if kind == "uniform" else 8
+    idx = np.stack([rng.permutation(pool)[:K] for _ in range(T)]).astype(np.int32)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    m_cap = M.moe_capacity_rows(T, E, K)
+    fill = lambda n, dt: torch.full(n, 0x3ead, dtype=dt, device=DEV)
+    out = dict(counts=fill((E,), torch.int32), offsets=fill((E + 1,), torch.int32),
+               row_of=fill((T, K), torch.int32), src_token=fill((m_cap,), torch.int32),
+               tile_expert=fill((m_cap // ALIGN,), torch.int32),
+               x_rows=torch.full((m_cap, H), 7.0, dtype=torch.bfloat16, device=DEV))
+    print(f"case: permute chunk boundary T {T} {kind}", flush=True)
+    p = M.moe_permute(torch.from_numpy(idx).to(DEV), x, E, out=out)
+    torch.cuda.synchronize()
+    M.moe_permute_check(p["status"])
+    ref = O.permute(idx, E, ALIGN)
+    g = {k: P.to_np(v) for k, v in p.items() if k not in ("x_rows", "status")}
+    P.check_permute(g, ref, E, ALIGN, m_cap)
+    rows = torch.from_numpy(ref["row_of"].reshape(-1)).to(DEV).long()
+    toks = torch.from_numpy(np.repeat(np.arange(T), K)).to(DEV).long()
+    assert torch.equal(p["x_rows"][rows], x[toks])
+
+
 @pytest.mark.parametrize("T", [700, 200])
 def test_permute_rejects_bad_ids(M, T):
     """The permutation's data check: tokens with an expert id outside [0,E)
