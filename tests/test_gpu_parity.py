@@ -224,6 +224,13 @@ MID = {
     # the router gradient through the normalised weights vanishes exactly
     "T333_H128_E1_K1": Workload("e1", T=333, H=128, E=1, K=1, S=1, F=96, seed=28,
                                 router_std=0.1),
+    # more than eight selected experts (the combine kernels' second
+    # instantiation), K not a power of two
+    "T300_H192_E40_K10": Workload("k10", T=300, H=192, E=40, K=10, S=1, F=96, seed=29,
+                                  router_std=0.1),
+    # the largest K the library takes, every expert selected by every token
+    "T260_H128_E16_K16": Workload("k16", T=260, H=128, E=16, K=16, S=2, F=64, seed=30,
+                                  router_std=0.1),
 }
 
 
