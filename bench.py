@@ -39,6 +39,10 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 # device copy (FETCH_SIZE reads half the bytes a copy moves: factor 2.0;
 # WRITE_SIZE reads them exactly: factor 1.0).  Valid only for the grouped-GEMM
 # source they were taken on, identified by its SHA-256; otherwise reported null.
+# HBM read rate of a plain streaming-read kernel on the MI355X (16-byte
+# non-temporal loads over 4 GiB, 1k-16k workgroups: 7.0-7.1 TB/s); reported
+# beside HBM-bound launches for context
+STREAM_READ_GBS = 7050.0
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "70b10f934d4993bfb73aa02c736f14f13c428271fc8e858beb58a582e1368446"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
@@ -78,7 +82,10 @@ def roofline_of(name, w, launch_ms, traffic=True, live=None):
              "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     else:
         r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-             "frac": round(gbs / PEAK_HBM_GBS, 4), "achieved_tflops": round(tf, 2)}
+             "frac": round(gbs / PEAK_HBM_GBS, 4), "achieved_tflops": round(tf, 2),
+             # context, not the peak: what plain streaming reads reach on this card
+             "reference_read_gbs": STREAM_READ_GBS,
+             "frac_of_reference_read": round(gbs / STREAM_READ_GBS, 4)}
     r.update({"kernel": f"grouped GEMM {name}", "launch_ms": round(launch_ms, 4),
               "flop_per_byte": round(flops / nbytes, 1), "algorithmic_gb": round(nbytes / 1e9, 3)})
     r.update(traffic_of(name, w) if traffic else {"traffic": None})
