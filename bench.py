@@ -46,12 +46,12 @@ STREAM_READ_GBS = 7050.0
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "70b10f934d4993bfb73aa02c736f14f13c428271fc8e858beb58a582e1368446"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3048512.1, 405504.1), "down_fwd": (1088823.2, 491541.3),
-    "shared_gate_up_fwd": (348246.7, 135202.4), "shared_down_fwd": (180295.2, 81937.6),
-    "down_dgrad": (1889009.6, 270336.3), "gate_up_dgrad": (2565813.0, 491521.8),
-    "down_wgrad": (322259.3, 1802310.5), "gate_up_wgrad": (846597.1, 3605101.3),
-    "shared_down_dgrad": (352424.2, 90118.6), "shared_gate_up_dgrad": (360523.3, 81921.0),
-    "shared_down_wgrad": (217238.5, 28160.5), "shared_gate_up_wgrad": (436486.5, 56320.0),
+    "gate_up_fwd": (3059185.9, 405504.1), "down_fwd": (1087437.7, 491521.0),
+    "shared_gate_up_fwd": (348246.7, 135193.8), "shared_down_fwd": (180295.2, 81931.0),
+    "down_dgrad": (1914870.1, 270336.0), "gate_up_dgrad": (2541261.3, 491524.8),
+    "down_wgrad": (321776.8, 1802328.8), "gate_up_wgrad": (847258.1, 3605156.3),
+    "shared_down_dgrad": (352634.4, 90114.9), "shared_gate_up_dgrad": (360523.5, 81920.5),
+    "shared_down_wgrad": (217241.2, 28160.2), "shared_gate_up_wgrad": (435313.4, 56320.2),
 }
 
 
