@@ -250,10 +250,10 @@ class Layer:
 
     def step_two_streams(self, side, backward=True):
         """The same step (no load balancing) with the independent launches on a
-        second stream, joined back through events: the shared experts'
-        products beside the router, permute and routed forward, and beside the
-        routed backward the shared data gradients and all weight gradients
-        (each as soon as its inputs exist).  Results are bit-identical to
+        second stream, joined back through events: the shared experts' whole
+        forward and backward (they need only x and dy) beside the router,
+        permute and routed forward, and the routed weight gradients beside the
+        routed data gradients (each as soon as its inputs exist).  Results are bit-identical to
         forward() + backward(); the launches share the card, so none of them
         can be timed alone here."""
         import torch
@@ -276,6 +276,8 @@ class Layer:
             if backward:
                 M.moe_grouped_down_dgrad(self.w2f, b["act_sh"], g["dy"], dact=b["dact_sh"])
                 M.moe_grouped_gate_up_dgrad(self.w1f, b["dact_sh"], dx_rows=b["dx_sh"])
+                M.moe_grouped_down_wgrad(g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"])
+                M.moe_grouped_gate_up_wgrad(b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"])
         M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
                     ws=b["route_ws"])
         M.moe_permute(b["topk_idx"], g["x"], E, out=p, ws=b["perm_ws"])
@@ -295,8 +297,6 @@ class Layer:
         side.wait_event(mark(main))
         with torch.cuda.stream(side):
             M.moe_grouped_gate_up_wgrad(b["dact"], p["x_rows"], E, *seg, dw1=b["dw1"])
-            M.moe_grouped_down_wgrad(g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"])
-            M.moe_grouped_gate_up_wgrad(b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"])
         M.moe_grouped_gate_up_dgrad(g["w1"], b["dact"], *seg, dx_rows=b["dx_rows"])
         M.moe_route_bwd(g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
                         p["offsets"], p["counts"], p["src_token"], dw_router=b["dw_router"],
@@ -735,10 +735,10 @@ def main():
         return marks[0].elapsed_time(marks[-1]) / args.steps, per
 
     # the step as the layer runs it: captured once as a HIP graph with the
-    # independent launches on a second stream (the shared experts' products
-    # beside the router, permute and routed forward; the shared data
-    # gradients and every weight gradient beside the routed data gradients),
-    # results bit-identical to the eager step.  Its replays are the timed
+    # independent launches on a second stream (the shared experts' forward
+    # and backward beside the router, permute and routed forward; the routed
+    # weight gradients beside the routed data gradients), results
+    # bit-identical to the eager step.  Its replays are the timed
     # region of the metric; the one-stream graph is timed beside it.
     graph_ms = None
     ms, step_ms, schedule = eager_ms, None, "eager, one stream"
