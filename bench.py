@@ -225,10 +225,12 @@ class Layer:
         self._gemm("shared_gate_up_wgrad", ev, lambda: M.moe_grouped_gate_up_wgrad(
             b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"]))
         if not balance:
-            self._gemm("route_bwd", ev, lambda: M.moe_route_bwd(
+            # router gradients and the un-permute in one call: the router's
+            # input gradient is added where dx is summed
+            self._gemm("route_permute_bwd", ev, lambda: M.moe_route_permute_bwd(
                 g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
-                p["offsets"], p["counts"], p["src_token"], dw_router=b["dw_router"],
-                dx_router=b["dx_router"], ws=b["rb_ws"]))
+                p["offsets"], p["counts"], p["src_token"], b["dx_rows"], b["dx_sh"],
+                dw_router=b["dw_router"], dx=b["dx"], ws=b["rb_ws"]))
         else:
             # the balance loss's dense logit gradient, the combine path's added
             # into it, and one dense router backward for both
@@ -239,8 +241,8 @@ class Layer:
             self._gemm("route_bwd_dense", ev, lambda: M.moe_route_bwd_dense(
                 g["x"], g["w_router"], b["dlogit_bal"], b["dw_router"], b["dx_router"],
                 ws=b["dense_ws"], accumulate=False))
-        self._gemm("permute_bwd", ev, lambda: M.moe_permute_bwd(
-            b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"]))
+            self._gemm("permute_bwd", ev, lambda: M.moe_permute_bwd(
+                b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"]))
         if balance:
             # the bias step on this batch's loads (a copy of the bias, so that
             # every timed step routes the same way)
@@ -276,6 +278,7 @@ class Layer:
             if backward:
                 M.moe_grouped_down_dgrad(self.w2f, b["act_sh"], g["dy"], dact=b["dact_sh"])
                 M.moe_grouped_gate_up_dgrad(self.w1f, b["dact_sh"], dx_rows=b["dx_sh"])
+                shared_dx = mark(side)
                 M.moe_grouped_down_wgrad(g["dy"], b["h_sh"], 1, dw2=b["dw2_sh"])
                 M.moe_grouped_gate_up_wgrad(b["dact_sh"], g["x"], 1, dw1=b["dw1_sh"])
         M.moe_route(g["x"], g["w_router"], g["bias"], K, b["topk_idx"], b["topk_w"], b["topk_s"],
@@ -298,15 +301,17 @@ class Layer:
         with torch.cuda.stream(side):
             M.moe_grouped_gate_up_wgrad(b["dact"], p["x_rows"], E, *seg, dw1=b["dw1"])
         M.moe_grouped_gate_up_dgrad(g["w1"], b["dact"], *seg, dx_rows=b["dx_rows"])
-        M.moe_route_bwd(g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"], p["row_of"],
-                        p["offsets"], p["counts"], p["src_token"], dw_router=b["dw_router"],
-                        dx_router=b["dx_router"], ws=b["rb_ws"])
+        # dx needs the shared experts' input gradient, not the weight gradients
+        main.wait_event(shared_dx)
+        M.moe_route_permute_bwd(g["x"], g["w_router"], b["topk_idx"], b["topk_s"], b["dg"],
+                                p["row_of"], p["offsets"], p["counts"], p["src_token"],
+                                b["dx_rows"], b["dx_sh"], dw_router=b["dw_router"], dx=b["dx"],
+                                ws=b["rb_ws"])
         main.wait_stream(side)
-        M.moe_permute_bwd(b["dx_rows"], p["row_of"], b["dx_sh"], b["dx_router"], dx=b["dx"])
 
 # the entry points around the grouped GEMMs, timed like them in the main loop
 ROW_OPS_FWD = ("route", "permute", "combine")
-ROW_OPS_BWD = ("combine_bwd", "route_bwd", "permute_bwd")
+ROW_OPS_BWD = ("combine_bwd", "route_permute_bwd")
 
 
 def row_op_bytes(w, name):
@@ -330,6 +335,8 @@ def row_op_bytes(w, name):
         return T * row + 4 * H * E + 16 * tk + 4 * m_cap + 4 * H * E + 4 * T * H
     if name == "permute_bwd":  # dx_rows, dx_shared, dx_router, row_of in; dx out
         return tk * row + (T * row if w.S else 0) + 4 * T * H + 4 * tk + T * row
+    if name == "route_permute_bwd":  # both, without dx_router's write and read (and row_of once)
+        return row_op_bytes(w, "route_bwd") + row_op_bytes(w, "permute_bwd") - 8 * T * H - 4 * tk
     raise KeyError(name)
 
 

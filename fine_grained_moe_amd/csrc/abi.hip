@@ -455,6 +455,30 @@ moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx
                     __func__);
 }
 
+moe_status_t moe_route_permute_bwd(int32_t T, int32_t H, int32_t E, int32_t K, const uint16_t* x,
+                                   const float* w_router, const int32_t* topk_idx,
+                                   const float* topk_s, const float* dg, const int32_t* row_of,
+                                   const int32_t* offsets, const int32_t* counts,
+                                   const int32_t* src_token, const uint16_t* dx_rows,
+                                   const uint16_t* dx_shared, float* dw_router, uint16_t* dx,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_dims(__func__, T, H, E, K);
+  if (st) return st;
+  REQUIRE(w_router && offsets && counts && dw_router, MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(T == 0 || (x && topk_idx && topk_s && dg && row_of && src_token && dx_rows && dx),
+          MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  REQUIRE(ws != nullptr && ws_bytes >= moe_route_bwd_workspace_bytes(T, H, E, K),
+          MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQUIRE_ALIGNED(x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token, dx_rows,
+                  dx_shared, dw_router, dx);
+  REQUIRE_WS_ALIGNED(ws);
+  return hip_status(moe::launch_route_permute_bwd(T, H, E, K, x, w_router, topk_idx, topk_s, dg,
+                                                  row_of, offsets, counts, src_token, dx_rows,
+                                                  dx_shared, dw_router, dx, ws,
+                                                  (hipStream_t)stream),
+                    __func__);
+}
+
 moe_status_t moe_bias_update(int32_t E, const int32_t* counts, float* bias, float gamma,
                              void* stream) {
   REQUIRE(E > 0, MOE_ERR_INVALID_ARGUMENT, "E <= 0");

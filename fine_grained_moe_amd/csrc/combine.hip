@@ -125,12 +125,18 @@ __global__ void __launch_bounds__(NT) combine_bwd_kernel(int T, int H, int K,
   }
 }
 
-template <int KMAX, int TPT>
+// ROUTER: dx_router is not read; the router's input gradient is formed here
+// from the route backward's workspace (wt = W_r^T, dl_row = the logit
+// gradient of every row), in the order route_bwd_token_kernel forms it
+template <int KMAX, int TPT, bool ROUTER>
 __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
                                                            const uint16_t* __restrict__ dx_rows,
                                                            const int32_t* __restrict__ row_of,
                                                            const uint16_t* __restrict__ dx_shared,
                                                            const float* __restrict__ dx_router,
+                                                           const float* __restrict__ wt,
+                                                           const float* __restrict__ dl_row,
+                                                           const int32_t* __restrict__ topk_idx,
                                                            uint16_t* __restrict__ dx) {
   const int lane = threadIdx.x % TPT;
   const int t = blockIdx.x * (NT / TPT) + threadIdx.x / TPT;
@@ -138,6 +144,13 @@ __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
   int rows[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) rows[k] = k < K ? row_of[(int64_t)t * K + k] : 0;
+  float dlk[KMAX];
+  int ek[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    dlk[k] = (ROUTER && k < K) ? dl_row[rows[k]] : 0.f;
+    ek[k] = (ROUTER && k < K) ? topk_idx[(int64_t)t * K + k] : 0;
+  }
   const int nchunk = H / 8;
   for (int c = lane; c < nchunk; c += TPT) {
     u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
@@ -146,7 +159,20 @@ __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
     for (int k = 0; k < KMAX; ++k)
       if (k < K) vr[k] = ((const u32x4*)(dx_rows + (int64_t)rows[k] * H))[c];
     if (dx_shared) vs = ((const u32x4*)(dx_shared + (int64_t)t * H))[c];
-    if (dx_router) {
+    if (ROUTER) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (k < K) {
+          const f32x4* w = (const f32x4*)(wt + (int64_t)ek[k] * H + (int64_t)c * 8);
+          const f32x4 w0 = w[0], w1 = w[1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a0[i] = __builtin_fmaf(dlk[k], w0[i], a0[i]);
+            a1[i] = __builtin_fmaf(dlk[k], w1[i], a1[i]);
+          }
+        }
+      }
+    } else if (dx_router) {
       const f32x4* p = (const f32x4*)(dx_router + (int64_t)t * H + (int64_t)c * 8);
       a0 = p[0];
       a1 = p[1];
@@ -226,6 +252,8 @@ __global__ void __launch_bounds__(NT) route_bwd_token_kernel(int T, int H, int E
   const float ds = (d - sdg / ssum) / ssum;
   const float dl = ds * s * (1.0f - s);
   if (lane < K) dl_row[row_of[(int64_t)t * K + lane]] = dl;
+  // without dx_router the un-permute forms the input gradient from dl_row
+  if (dx_router == nullptr) return;
   float dlk[16];
   int ek[16];
   for (int k = 0; k < K; ++k) {
@@ -329,18 +357,33 @@ hipError_t launch_combine_bwd(int T, int H, int K, const uint16_t* dy, const uin
   return hipGetLastError();
 }
 
+static hipError_t unpermute(int T, int H, int K, const uint16_t* dx_rows, const int32_t* row_of,
+                            const uint16_t* dx_shared, const float* dx_router, const float* wt,
+                            const float* dl_row, const int32_t* topk_idx, uint16_t* dx,
+                            hipStream_t s) {
+  constexpr int TPT = MOE_ROW_TPT, TPB = comb::NT / TPT;
+  const dim3 grid((T + TPB - 1) / TPB);
+  const bool router = wt != nullptr;
+  if (K <= 8 && !router)
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<8, TPT, false>), grid, dim3(comb::NT), 0, s, T,
+                       H, K, dx_rows, row_of, dx_shared, dx_router, wt, dl_row, topk_idx, dx);
+  else if (K <= 8)
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<8, TPT, true>), grid, dim3(comb::NT), 0, s, T,
+                       H, K, dx_rows, row_of, dx_shared, dx_router, wt, dl_row, topk_idx, dx);
+  else if (!router)
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<16, TPT, false>), grid, dim3(comb::NT), 0, s, T,
+                       H, K, dx_rows, row_of, dx_shared, dx_router, wt, dl_row, topk_idx, dx);
+  else
+    hipLaunchKernelGGL((comb::unpermute_add_kernel<16, TPT, true>), grid, dim3(comb::NT), 0, s, T,
+                       H, K, dx_rows, row_of, dx_shared, dx_router, wt, dl_row, topk_idx, dx);
+  return hipGetLastError();
+}
+
 hipError_t launch_unpermute_add(int T, int H, int K, const uint16_t* dx_rows,
                                 const int32_t* row_of, const uint16_t* dx_shared,
                                 const float* dx_router, uint16_t* dx, hipStream_t s) {
-  constexpr int TPT = MOE_ROW_TPT, TPB = comb::NT / TPT;
-  const dim3 grid((T + TPB - 1) / TPB);
-  if (K <= 8)
-    hipLaunchKernelGGL((comb::unpermute_add_kernel<8, TPT>), grid, dim3(comb::NT), 0, s, T, H, K,
-                       dx_rows, row_of, dx_shared, dx_router, dx);
-  else
-    hipLaunchKernelGGL((comb::unpermute_add_kernel<16, TPT>), grid, dim3(comb::NT), 0, s, T, H, K,
-                       dx_rows, row_of, dx_shared, dx_router, dx);
-  return hipGetLastError();
+  return unpermute(T, H, K, dx_rows, row_of, dx_shared, dx_router, nullptr, nullptr, nullptr, dx,
+                   s);
 }
 
 size_t route_bwd_workspace_bytes(int64_t m_cap, int H, int E) {
@@ -365,6 +408,24 @@ hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x,
   hipLaunchKernelGGL(comb::route_bwd_wgrad_kernel, dim3((H + comb::WG_COLS - 1) / comb::WG_COLS, E),
                      dim3(256), 0, s, H, E, x, src_token, dl_row, offsets, counts, dw_router);
   return hipGetLastError();
+}
+
+hipError_t launch_route_permute_bwd(int T, int H, int E, int K, const uint16_t* x,
+                                    const float* w_router, const int32_t* topk_idx,
+                                    const float* topk_s, const float* dg, const int32_t* row_of,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* src_token, const uint16_t* dx_rows,
+                                    const uint16_t* dx_shared, float* dw_router, uint16_t* dx,
+                                    void* ws, hipStream_t s) {
+  // the router backward without its [T,H] input gradient (dl_row and W_r^T
+  // stay in ws), then the un-permute forming that gradient where it adds it
+  hipError_t e = launch_route_bwd(T, H, E, K, x, w_router, topk_idx, topk_s, dg, row_of, offsets,
+                                  counts, src_token, dw_router, nullptr, ws, s);
+  if (e != hipSuccess || T == 0) return e;
+  const float* wt = (const float*)ws;
+  const float* dl_row =
+      (const float*)((const char*)ws + ((size_t)E * H * sizeof(float) + 255) / 256 * 256);
+  return unpermute(T, H, K, dx_rows, row_of, dx_shared, nullptr, wt, dl_row, topk_idx, dx, s);
 }
 
 }  // namespace moe

@@ -83,6 +83,15 @@ hipError_t launch_route_bwd(int T, int H, int E, int K, const uint16_t* x,
                             const float* dg, const int32_t* row_of, const int32_t* offsets,
                             const int32_t* counts, const int32_t* src_token, float* dw_router,
                             float* dx_router, void* ws, hipStream_t s);
+// launch_route_bwd without materialising dx_router, then the un-permute-add
+// with the router's input gradient formed from ws
+hipError_t launch_route_permute_bwd(int T, int H, int E, int K, const uint16_t* x,
+                                    const float* w_router, const int32_t* topk_idx,
+                                    const float* topk_s, const float* dg, const int32_t* row_of,
+                                    const int32_t* offsets, const int32_t* counts,
+                                    const int32_t* src_token, const uint16_t* dx_rows,
+                                    const uint16_t* dx_shared, float* dw_router, uint16_t* dx,
+                                    void* ws, hipStream_t s);
 
 
 hipError_t launch_bias_update(int E, const int32_t* counts, float* bias, float gamma,

@@ -57,6 +57,8 @@ _SIGS = {
     "moe_route_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                              _p, _sz, _p]),
     "moe_permute_bwd": (_i32, [_i32, _i32, _i32, _p, _p, _p, _p, _p, _p]),
+    "moe_route_permute_bwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, _p, _p, _p, _p, _sz, _p]),
     "moe_bias_update": (_i32, [_i32, _p, _p, ctypes.c_float, _p]),
     "moe_seq_balance_fwd": (_i32, [_i32, _i32, _i32, _i32, _p, _p, ctypes.c_float, _p, _p, _p, _sz,
                                    _p]),
@@ -490,6 +492,37 @@ def moe_permute_bwd(dx_rows, row_of, dx_shared=None, dx_router=None, dx=None):
                                 _ptr(dx_shared, BF16, "dx_shared"), _ptr(dx_router, F32, "dx_router"),
                                 _ptr(dx, BF16, "dx"), _stream()))
     return dx
+
+
+def moe_route_permute_bwd(x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token,
+                          dx_rows, dx_shared=None, dw_router=None, dx=None, ws=None):
+    """moe_route_bwd then moe_permute_bwd in one call, the router's input
+    gradient added where dx is summed.  Returns (dw_router [H,E] fp32,
+    dx [T,H] bf16), bit-identical to the two calls."""
+    T, K = topk_idx.shape
+    H, E = w_router.shape
+    dev = w_router.device
+    dw_router = torch.empty((H, E), dtype=F32, device=dev) if dw_router is None else dw_router
+    dx = torch.empty((T, H), dtype=BF16, device=dev) if dx is None else dx
+    nbytes = moe_route_bwd_workspace_bytes(T, H, E, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if ws is None else ws
+    _expect(x=(x, (T, H)), topk_s=(topk_s, (T, K)), dg=(dg, (T, K)), row_of=(row_of, (T, K)),
+            offsets=(offsets, (E + 1,)), counts=(counts, (E,)),
+            src_token=(src_token, (src_token.shape[0],) if src_token is not None else ()),
+            dx_rows=(dx_rows, (dx_rows.shape[0], H) if dx_rows is not None else ()),
+            dx_shared=(dx_shared, (T, H)), dw_router=(dw_router, (H, E)), dx=(dx, (T, H)))
+    if src_token is not None and src_token.shape[0] < moe_capacity_rows(T, E, K):
+        raise ValueError("src_token must hold at least moe_capacity_rows(T, E, K) entries")
+    _check(_lib.moe_route_permute_bwd(T, H, E, K, _ptr(x, BF16, "x"),
+                                      _ptr(w_router, F32, "w_router"), _ptr(topk_idx, I32, "topk_idx"),
+                                      _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
+                                      _ptr(row_of, I32, "row_of"), _ptr(offsets, I32, "offsets"),
+                                      _ptr(counts, I32, "counts"), _ptr(src_token, I32, "src_token"),
+                                      _ptr(dx_rows, BF16, "dx_rows"),
+                                      _ptr(dx_shared, BF16, "dx_shared"),
+                                      _ptr(dw_router, F32, "dw_router"), _ptr(dx, BF16, "dx"),
+                                      _ptr(ws), ws.numel(), _stream()))
+    return dw_router, dx
 
 
 def moe_bias_update(counts, bias, gamma):

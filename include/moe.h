@@ -392,6 +392,27 @@ moe_status_t moe_permute_bwd(int32_t T, int32_t H, int32_t K, const uint16_t* dx
                              const float* dx_router, uint16_t* dx, void* stream);
 
 /*
+ * moe_route_permute_bwd - moe_route_bwd followed by moe_permute_bwd (the
+ * backward timed in the Technical Report summary, "Results", routing held
+ * fixed), with the router's input gradient added where dx is summed instead
+ * of passing through a [T,H] fp32 buffer:
+ *   dw_router as moe_route_bwd computes it;
+ *   dx[t,:] = sum_k dx_rows[row_of[t,k],:] + dx_shared[t,:] + dx_router[t,:]
+ * with dx_router[t,:] formed on the fly exactly as moe_route_bwd forms it, so
+ * both outputs equal those of the two calls bit for bit.  Arguments as for
+ * the two calls (dx_shared nullable); ws: device workspace of at least
+ * moe_route_bwd_workspace_bytes(T,H,E,K) bytes.
+ */
+moe_status_t moe_route_permute_bwd(int32_t T, int32_t H, int32_t E, int32_t K,
+                                   const uint16_t* x, const float* w_router,
+                                   const int32_t* topk_idx, const float* topk_s, const float* dg,
+                                   const int32_t* row_of, const int32_t* offsets,
+                                   const int32_t* counts, const int32_t* src_token,
+                                   const uint16_t* dx_rows, const uint16_t* dx_shared,
+                                   float* dw_router, uint16_t* dx, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
  * Load balancing.  Technical Report summary, "Method": balancing by DeepSeek's
  * auxiliary-loss-free bias update, complemented by a sequence-wise balance
  * loss; model card, "Model Architecture Features": dynamic bias terms.  The

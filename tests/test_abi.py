@@ -153,6 +153,21 @@ def test_route_bwd_rejects(lib):
     assert f(16, 64, 8, 2, *[_p(FAKE)] * 8, _p(None), *[_p(FAKE)] * 3, 1 << 30, _p(None)) == 1  # src_token
 
 
+def test_route_permute_bwd_rejects(lib):
+    f = lib.moe_route_permute_bwd
+    # x, w_router, topk_idx, topk_s, dg, row_of, offsets, counts, src_token, dx_rows,
+    # dx_shared, dw_router, dx, ws, ws_bytes, stream
+    f.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 14 + [ctypes.c_size_t, ctypes.c_void_p]
+    big = 1 << 30
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 14, 16, _p(None)) == 3                  # workspace
+    assert f(16, 64, 8, 2, _p(None), *[_p(FAKE)] * 13, big, _p(None)) == 1        # null x
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 9, _p(None), *[_p(FAKE)] * 4, big, _p(None)) == 1  # dx_rows
+    assert f(16, 64, 8, 2, *[_p(FAKE)] * 12, _p(None), _p(FAKE), big, _p(None)) == 1  # null dx
+    assert f(16, 60, 8, 2, *[_p(FAKE)] * 14, big, _p(None)) == 2                  # H % 64
+    assert f(16, 64, 8, 9, *[_p(FAKE)] * 14, big, _p(None)) != 0                  # K > E
+    assert f(16, 64, 8, 2, *[_p(FAKE + 2)] * 14, big, _p(None)) == 1              # misaligned
+
+
 def test_backward_steps_reject(lib):
     # (name, number of operand pointers after the three segment pointers)
     for name, nptr in (("moe_grouped_down_dgrad", 4), ("moe_grouped_down_wgrad", 3),

@@ -17,12 +17,13 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-# buffers the step writes in full
-OUTPUTS = ("y", "dx", "dw1", "dw2", "dw1_sh", "dw2_sh", "dw_router", "dx_router", "dg",
+# buffers the step writes in full (the router's [T,H] input gradient only
+# with load balancing: without it that gradient is added inside the un-permute)
+OUTPUTS = ("y", "dx", "dw1", "dw2", "dw1_sh", "dw2_sh", "dw_router", "dg",
            "act_sh", "dact_sh", "topk_idx", "topk_w", "topk_s")
 # row buffers of the routed path: pad rows are never written, only valid rows compare
 ROWS = ("act", "h", "y_rows", "dy_rows", "dact", "dx_rows")
-BALANCE_OUTPUTS = ("loss", "seq_f", "dlogit_bal", "scores", "bias_train")
+BALANCE_OUTPUTS = ("loss", "seq_f", "dlogit_bal", "scores", "bias_train", "dx_router")
 
 
 @pytest.fixture(scope="module")

@@ -302,6 +302,34 @@ def test_backward_steps_match_composite(M):
     assert torch.equal(dw1_sh, grads["dw1_sh"]) and torch.equal(dw2_sh, grads["dw2_sh"])
 
 
+def _fused_route_permute(M, ctx, grads):
+    p = ctx["perm"]
+    return M.moe_route_permute_bwd(ctx["x"], ctx["w_router"], ctx["topk_idx"], ctx["topk_s"],
+                                   grads["dg"], p["row_of"], p["offsets"], p["counts"],
+                                   p["src_token"], grads["dx_rows"], grads["dx_shared"])
+
+
+@pytest.mark.parametrize("name", ["T1000_H512_E16_K4_F352", "T300_H128_E8_K1_S0", "T1_H256_E32_K6",
+                                  "T300_H192_E40_K10", "T260_H128_E16_K16", "fwdbwd"])
+def test_route_permute_bwd_matches_two_calls(M, name):
+    """moe_route_permute_bwd (the router's input gradient formed inside the
+    un-permute) gives dW_r and dx bit for bit equal to moe_route_bwd followed
+    by moe_permute_bwd, with and without shared experts, K up to 16, and at
+    dots.llm1 shapes (T = 8192)."""
+    if name == "fwdbwd":
+        w = WORKLOADS["fwdbwd"]
+        g = generate_torch(w, torch.device(DEV), with_dy=True)
+    else:
+        w = MID[name]
+        g = to_gpu(generate_numpy(w, with_dy=True))
+    print(f"route_permute_bwd {name}: T={w.T} H={w.H} E={w.E} K={w.K} S={w.S}", flush=True)
+    y, ctx, grads = run_layer(M, g, w.K, True)
+    dwr, dx = _fused_route_permute(M, ctx, grads)
+    torch.cuda.synchronize()
+    assert torch.equal(dwr, grads["dw_router"])
+    assert torch.equal(dx, grads["dx"])
+
+
 def test_empty_batch(M):
     E, K, H, F = 8, 2, 64, 32
     x = torch.zeros((0, H), dtype=torch.bfloat16, device=DEV)
@@ -321,8 +349,12 @@ def test_empty_batch(M):
     dg = torch.zeros((0, K), device=DEV)
     dwr, dxr = M.moe_route_bwd(x, wr, idx, ts, dg, p["row_of"], p["offsets"], p["counts"],
                                p["src_token"])
+    dx_rows = torch.zeros((p["x_rows"].shape[0], H), dtype=torch.bfloat16, device=DEV)
+    dwr2, dx2 = M.moe_route_permute_bwd(x, wr, idx, ts, dg, p["row_of"], p["offsets"],
+                                        p["counts"], p["src_token"], dx_rows)
     torch.cuda.synchronize()
     assert (dw1 == 0).all() and (dw2 == 0).all() and (dwr == 0).all()
+    assert (dwr2 == 0).all() and dx2.shape == (0, H)
 
 
 @pytest.mark.parametrize("T,kind", [(1, "uniform"), (255, "uniform"), (256, "uniform"),
