@@ -231,6 +231,13 @@ MID = {
     # the largest K the library takes, every expert selected by every token
     "T260_H128_E16_K16": Workload("k16", T=260, H=128, E=16, K=16, S=2, F=64, seed=30,
                                   router_std=0.1),
+    # a decode-like batch: at most 8 rows in any expert's 128-row tile
+    "T40_H256_E64_K6_F160": Workload("few-rows", T=40, H=256, E=64, K=6, S=2, F=160, seed=33,
+                                     router_std=0.1),
+    # Zipf-skewed at a small batch: four experts hold all 150 tokens (two row
+    # tiles each, the second ragged), the other 60 none
+    "T150_H192_E64_K4_F96_skew": Workload("skew-k4", T=150, H=192, E=64, K=4, S=1, F=96,
+                                          seed=34, bias_kind="zipf", router_std=0.02),
 }
 
 
