@@ -44,14 +44,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 # beside HBM-bound launches for context
 STREAM_READ_GBS = 7050.0
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "70b10f934d4993bfb73aa02c736f14f13c428271fc8e858beb58a582e1368446"
+TRAFFIC_SOURCE_SHA256 = "912afe55cfbeb68c8f566f90f0a3a7eb6ccf42331a5981c668b8a2c55e682a10"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3059185.9, 405504.1), "down_fwd": (1087437.7, 491521.0),
-    "shared_gate_up_fwd": (348246.7, 135193.8), "shared_down_fwd": (180295.2, 81931.0),
-    "down_dgrad": (1914870.1, 270336.0), "gate_up_dgrad": (2541261.3, 491524.8),
-    "down_wgrad": (321776.8, 1802328.8), "gate_up_wgrad": (847258.1, 3605156.3),
-    "shared_down_dgrad": (352634.4, 90114.9), "shared_gate_up_dgrad": (360523.5, 81920.5),
-    "shared_down_wgrad": (217241.2, 28160.2), "shared_gate_up_wgrad": (435313.4, 56320.2),
+    "gate_up_fwd": (3056198.4, 405504.2), "down_fwd": (1081080.9, 491526.4),
+    "shared_gate_up_fwd": (348246.7, 135221.8), "shared_down_fwd": (180295.2, 81954.7),
+    "down_dgrad": (1899794.6, 270336.0), "gate_up_dgrad": (2545606.8, 491525.3),
+    "down_wgrad": (322394.6, 1802310.8), "gate_up_wgrad": (846636.6, 3605081.8),
+    "shared_down_dgrad": (352381.6, 90141.4), "shared_gate_up_dgrad": (360523.3, 81936.8),
+    "shared_down_wgrad": (217164.8, 28161.8), "shared_gate_up_wgrad": (434253.8, 56321.5),
 }
 
 

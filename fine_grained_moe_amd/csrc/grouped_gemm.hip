@@ -130,6 +130,8 @@ struct Args {
   int acc_out;           // F32: add to Cf instead of writing it
   int ksplit;            // F32, dense MGROUP: slices of the k range (0 or 1: none)
   int64_t split_stride;  // F32 with ksplit > 1: elements between slices' outputs
+  int kg_chunk;          // KGROUP: logical tiles per chunk dealt round-robin to the XCDs
+  int kg_tiles;          // KGROUP with kg_chunk: logical tiles (the grid is padded)
 };
 
 // MN-contig tile of BK k-rows x C columns.  A 1 KB region holds KPR k-rows.
@@ -233,8 +235,20 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   constexpr bool SPLIT = EPI == EPI_F32 && MODE == MGROUP;
   const int ks = (SPLIT && a.ksplit > 1) ? a.ksplit : 1;
   const int ntiles_live = (MODE == MGROUP) ? n_mt * a.n_ntiles * ks : (int)gridDim.x;
-  if ((int)blockIdx.x >= ntiles_live) return;
-  const int L0 = xcd_remap(blockIdx.x, ntiles_live);
+  int L0;
+  if (MODE == KGROUP && a.kg_chunk > 0) {
+    // chunks of kg_chunk consecutive logical tiles go to the XCDs in turn
+    // (the hardware hands consecutive workgroup ids to consecutive XCDs), so
+    // that a few experts holding most rows still spread over all of them;
+    // the grid is padded to whole rounds of chunks
+    const int CH = a.kg_chunk;
+    const int xcd = (int)blockIdx.x % kNumXcd, slot = (int)blockIdx.x / kNumXcd;
+    L0 = ((slot / CH) * kNumXcd + xcd) * CH + slot % CH;
+    if (L0 >= a.kg_tiles) return;
+  } else {
+    if ((int)blockIdx.x >= ntiles_live) return;
+    L0 = xcd_remap(blockIdx.x, ntiles_live);
+  }
   const int sp = SPLIT ? L0 / (n_mt * a.n_ntiles) : 0;
   const int L = SPLIT ? L0 - sp * (n_mt * a.n_ntiles) : L0;
   int e, mt, nt;
@@ -896,6 +910,27 @@ hipError_t launch_gemm_dgrad_up(int G, int64_t m_rows, int H, int F, const int32
   return launch_rows<KC, MC, EPI_STORE, CfgRowsN>(a, CfgRowsN::BN, CfgWide::BN, H, s);
 }
 
+// K-grouped launch over G experts' n_mtiles x n_ntiles tiles each.  The
+// experts' tile ranges (chunks of the logical order) go to the XCDs in turn:
+// with the whole range split into eight contiguous parts instead, a batch
+// whose rows sit in a few experts ran on one XCD (the Zipf-skewed T = 16384
+// batch's weight gradients: 22.5 ms, against 6.2 ms with the chunks), while
+// each expert's tiles still share one L2 (T = 8192 and the expert-parallel
+// shard: within 0.3 % of the contiguous split or faster).  Chunks of two
+// m-groups balanced the skewed batch better (5.6 ms) but cost the balanced
+// one 0.5 %.  A single group (the shared experts) keeps the contiguous split.
+template <int EPI>
+static hipError_t launch_kgroup(Args a, hipStream_t s) {
+  const int tiles = a.G * a.n_mtiles * a.n_ntiles;
+  if (a.G == 1) return launch<CfgWgrad, MC, MC, EPI, KGROUP>(a, tiles, s);
+  const int ch = a.n_mtiles * a.n_ntiles;  // one expert
+  const int cap = (tiles + 4 * kNumXcd - 1) / (4 * kNumXcd);  // at least four chunks per XCD
+  a.kg_chunk = ch < cap ? ch : cap;
+  a.kg_tiles = tiles;
+  const int span = kNumXcd * a.kg_chunk;
+  return launch<CfgWgrad, MC, MC, EPI, KGROUP>(a, (tiles + span - 1) / span * span, s);
+}
+
 // dW2[g] [H,F] = dy_rows_g^T [H, rows] . h_g [rows, F]
 hipError_t launch_gemm_wgrad_down(int G, int64_t m_rows, int H, int F, const int32_t* offsets,
                                   const int32_t* counts, const uint16_t* dy_rows,
@@ -907,7 +942,7 @@ hipError_t launch_gemm_wgrad_down(int G, int64_t m_rows, int H, int F, const int
   a.lda = H; a.ldb = F; a.ldc = F; a.strideB = 0; a.strideC = (int64_t)H * F;
   a.n_mtiles = (H + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (F + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
-  return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  return launch_kgroup<EPI_STORE>(a, s);
 }
 
 // dW1[g] [2F,H] = dact_g^T [2F, rows] . x_rows_g [rows, H]
@@ -921,7 +956,7 @@ hipError_t launch_gemm_wgrad_up(int G, int64_t m_rows, int H, int F, const int32
   a.lda = 2 * F; a.ldb = H; a.ldc = H; a.strideB = 0; a.strideC = (int64_t)2 * F * H;
   a.n_mtiles = (2 * F + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (H + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
-  return launch<CfgWgrad, MC, MC, EPI_STORE, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  return launch_kgroup<EPI_STORE>(a, s);
 }
 
 size_t dense_fwd_split_workspace_bytes(int64_t m_rows, int H, int F) {
@@ -983,7 +1018,7 @@ hipError_t launch_gemm_f32_tn_grouped(int G, const int32_t* offsets, const int32
   a.lda = lda; a.ldb = ldb; a.ldc = ldc; a.strideB = 0; a.strideC = strideC;
   a.n_mtiles = (M + CfgWgrad::BM - 1) / CfgWgrad::BM; a.n_ntiles = (N + CfgWgrad::BN - 1) / CfgWgrad::BN;
   a.G = G;
-  return launch<CfgWgrad, MC, MC, EPI_F32, KGROUP>(a, G * a.n_mtiles * a.n_ntiles, s);
+  return launch_kgroup<EPI_F32>(a, s);
 }
 
 }  // namespace moe
