@@ -644,10 +644,14 @@ def layer_forward(x, w_router, bias, w1, w2, w1_shf, w2_shf, K, save_for_backwar
     return y, ctx
 
 
-def layer_backward(dy, ctx, dloss=None):
+def layer_backward(dy, ctx, dloss=None, router_input_grad=False):
     """Backward of the MoE layer (dloss: upstream gradient of the balance
     loss, fp32 [1] device tensor, None = 1).  Returns dict(dx, dw1, dw2,
-    dw1_sh, dw2_sh, dw_router) plus the intermediates."""
+    dw1_sh, dw2_sh, dw_router) plus the intermediates.  Without the balance
+    loss the router's input gradient is added inside the un-permute
+    (moe_route_permute_bwd) and the intermediate dx_router is None, unless
+    router_input_grad asks for it (moe_route_bwd, then moe_permute_bwd; the
+    same dx and dw_router bit for bit)."""
     p = ctx["perm"]
     dy_rows, dg = moe_combine_bwd(dy, ctx["y_rows"], p["row_of"], ctx["topk_w"])
     dact, dx_rows, dw1, dw2 = moe_grouped_swiglu_bwd(p["x_rows"], ctx["w1"], ctx["w2"], ctx["act"],
@@ -658,6 +662,13 @@ def layer_backward(dy, ctx, dloss=None):
         _, dx_sh, dw1_sh, dw2_sh = moe_grouped_swiglu_bwd(ctx["x"], ctx["w1_shf"], ctx["w2_shf"],
                                                           ctx["act_sh"], ctx["h_sh"], dy)
     dlogit_bal = dlogit = None
+    if ctx.get("balance") is None and not router_input_grad:
+        dw_router, dx = moe_route_permute_bwd(ctx["x"], ctx["w_router"], ctx["topk_idx"],
+                                              ctx["topk_s"], dg, p["row_of"], p["offsets"],
+                                              p["counts"], p["src_token"], dx_rows, dx_sh)
+        return dict(dx=dx, dw1=dw1, dw2=dw2, dw1_sh=dw1_sh, dw2_sh=dw2_sh, dw_router=dw_router,
+                    dg=dg, dy_rows=dy_rows, dact=dact, dx_rows=dx_rows, dx_shared=dx_sh,
+                    dx_router=None, dlogit_balance=None, dlogit=None)
     if ctx.get("balance") is None:
         dw_router, dx_router = moe_route_bwd(ctx["x"], ctx["w_router"], ctx["topk_idx"],
                                              ctx["topk_s"], dg, p["row_of"], p["offsets"],

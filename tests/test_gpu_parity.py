@@ -76,9 +76,11 @@ def to_gpu(inp):
 
 
 def run_layer(M, g, K, backward):
+    """The layer forward and backward; the backward keeps the router's input
+    gradient as an intermediate, so that it can be compared with the oracle."""
     w1f, w2f = M.fuse_shared(g["w1_sh"], g["w2_sh"]) if g["w1_sh"].shape[0] > 0 else (None, None)
     y, ctx = M.layer_forward(g["x"], g["w_router"], g["bias"], g["w1"], g["w2"], w1f, w2f, K)
-    grads = M.layer_backward(g["dy"], ctx) if backward else None
+    grads = M.layer_backward(g["dy"], ctx, router_input_grad=True) if backward else None
     torch.cuda.synchronize()
     return y, ctx, grads
 
@@ -332,9 +334,14 @@ def test_route_permute_bwd_matches_two_calls(M, name):
     print(f"route_permute_bwd {name}: T={w.T} H={w.H} E={w.E} K={w.K} S={w.S}", flush=True)
     y, ctx, grads = run_layer(M, g, w.K, True)
     dwr, dx = _fused_route_permute(M, ctx, grads)
+    # the layer's default backward takes the fused call
+    fused = M.layer_backward(g["dy"], ctx)
     torch.cuda.synchronize()
     assert torch.equal(dwr, grads["dw_router"])
     assert torch.equal(dx, grads["dx"])
+    assert fused["dx_router"] is None
+    for n in ("dx", "dw_router", "dw1", "dw2"):
+        assert torch.equal(fused[n], grads[n]), n
 
 
 def test_empty_batch(M):
