@@ -513,6 +513,8 @@ def moe_route_permute_bwd(x, w_router, topk_idx, topk_s, dg, row_of, offsets, co
             dx_shared=(dx_shared, (T, H)), dw_router=(dw_router, (H, E)), dx=(dx, (T, H)))
     if src_token is not None and src_token.shape[0] < moe_capacity_rows(T, E, K):
         raise ValueError("src_token must hold at least moe_capacity_rows(T, E, K) entries")
+    if dx_rows is not None and dx_rows.shape[0] < moe_capacity_rows(T, E, K):
+        raise ValueError("dx_rows must hold at least moe_capacity_rows(T, E, K) rows")
     _check(_lib.moe_route_permute_bwd(T, H, E, K, _ptr(x, BF16, "x"),
                                       _ptr(w_router, F32, "w_router"), _ptr(topk_idx, I32, "topk_idx"),
                                       _ptr(topk_s, F32, "topk_s"), _ptr(dg, F32, "dg"),
