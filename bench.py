@@ -44,14 +44,14 @@ BALANCE_OPS = ("seq_loss_fwd", "seq_loss_bwd", "route_dlogit", "route_bwd_dense"
 # beside HBM-bound launches for context
 STREAM_READ_GBS = 7050.0
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
-TRAFFIC_SOURCE_SHA256 = "912afe55cfbeb68c8f566f90f0a3a7eb6ccf42331a5981c668b8a2c55e682a10"
+TRAFFIC_SOURCE_SHA256 = "7341e5ef1c3bf94b9fc07a151537583e70a8a6e4109d133897c7c703e29e1c04"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3056198.4, 405504.2), "down_fwd": (1081080.9, 491526.4),
-    "shared_gate_up_fwd": (348246.7, 135221.8), "shared_down_fwd": (180295.2, 81954.7),
-    "down_dgrad": (1899794.6, 270336.0), "gate_up_dgrad": (2545606.8, 491525.3),
-    "down_wgrad": (322394.6, 1802310.8), "gate_up_wgrad": (846636.6, 3605081.8),
-    "shared_down_dgrad": (352381.6, 90141.4), "shared_gate_up_dgrad": (360523.3, 81936.8),
-    "shared_down_wgrad": (217164.8, 28161.8), "shared_gate_up_wgrad": (434253.8, 56321.5),
+    "gate_up_fwd": (3072721.2, 405504.2), "down_fwd": (1087008.6, 491542.5),
+    "shared_gate_up_fwd": (348244.2, 135209.5), "shared_down_fwd": (180295.2, 81941.6),
+    "down_dgrad": (1879979.6, 270336.0), "gate_up_dgrad": (2554905.7, 491528.4),
+    "down_wgrad": (322414.0, 1802299.9), "gate_up_wgrad": (847144.8, 3605095.6),
+    "shared_down_dgrad": (352414.8, 90120.5), "shared_gate_up_dgrad": (360515.4, 81934.7),
+    "shared_down_wgrad": (217164.8, 28160.8), "shared_gate_up_wgrad": (434253.9, 56320.6),
 }
 
 

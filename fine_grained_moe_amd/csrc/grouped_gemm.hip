@@ -214,7 +214,9 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 // --------------------------------------------------------------------------
 // The kernel
 // --------------------------------------------------------------------------
-template <class Cfg, int ASRC, int BSRC, int EPI, int MODE>
+// NTB: the B operand's loads are non-temporal (a weight matrix that every
+// tile reads once: routed forward products at a few rows per expert)
+template <class Cfg, int ASRC, int BSRC, int EPI, int MODE, bool NTB = false>
 __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NW = Cfg::NW, STAGES = Cfg::STAGES;
   constexpr int WM = Cfg::WM, WN = Cfg::WN, WTM = Cfg::WTM, WTN = Cfg::WTN;
@@ -379,7 +381,7 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
       const int j = i - A_PER;
       if constexpr (BSRC == KC) {
         if constexpr (SPLIT) lb_kc.issue(rB, Bs, wave, j, kt + kofs, kend);
-        else lb_kc.issue(rB, Bs, wave, j, kt, a.K);
+        else lb_kc.template issue<NTB>(rB, Bs, wave, j, kt, a.K);
       } else if constexpr (MODE == MGROUP) {
         lb_mc.issue(rB, Bs, wave, j, kt, [&](int k) -> uint32_t {
           return k < a.K ? (uint32_t)k * a.ldb * 2 : kOOB;
@@ -746,11 +748,11 @@ __global__ void __launch_bounds__(Cfg::NT, Cfg::MINB) grouped_gemm_kernel(Args a
   }
 }
 
-template <class Cfg, int ASRC, int BSRC, int EPI, int MODE>
+template <class Cfg, int ASRC, int BSRC, int EPI, int MODE, bool NTB = false>
 static hipError_t launch(const Args& a, int nblocks, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<Cfg, ASRC, BSRC, EPI, MODE>), dim3(nblocks), dim3(Cfg::NT),
-                     0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<Cfg, ASRC, BSRC, EPI, MODE, NTB>), dim3(nblocks),
+                     dim3(Cfg::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -765,6 +767,16 @@ static hipError_t launch_rows(Args a, int n_cols_per_tile_rows, int n_cols_per_t
   auto rows = [&]() {
     a.n_mtiles = (int)((a.m_rows + CR::BM - 1) / CR::BM);
     a.n_ntiles = (ncols + n_cols_per_tile_rows - 1) / n_cols_per_tile_rows;
+    if constexpr (BSRC == KC && EPI != EPI_F32) {
+      // routed forward products at one row tile per expert or fewer on
+      // average (m_rows is the padded capacity, at most G*(kAlign-1) rows
+      // above the routed ones) read each weight slice about once: its loads
+      // go non-temporal (T = 256: gate/up and down 9 % and 8 % faster; where
+      // several row tiles share a weight slice, non-temporal weight loads
+      // cost 3-16 %: T = 8192 and the skewed T = 16384 batch)
+      if (a.tile_expert && a.m_rows - (int64_t)a.G * (kAlign - 1) <= (int64_t)kAlign * a.G)
+        return launch<CR, ASRC, BSRC, EPI, MGROUP, true>(a, a.n_mtiles * a.n_ntiles, s);
+    }
     return launch<CR, ASRC, BSRC, EPI, MGROUP>(a, a.n_mtiles * a.n_ntiles, s);
   };
   if constexpr (EPI == EPI_SWIGLU_BWD) {

@@ -41,7 +41,9 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // does not treat the LDS writes as aliasing every later LDS read (it would put
 // a wait for all outstanding loads before each transposing read); the kernel
 // orders them itself with explicit vmcnt waits and barriers.  M0 is used by
-// nothing else in these kernels.
+// nothing else in these kernels.  NT marks the load non-temporal (streamed:
+// for an operand every line of which is read once).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const u32x4& rs_in, uint32_t lds, uint32_t voff) {
   // both are workgroup-uniform; readfirstlane keeps them in SGPRs whatever
   // the compiler concluded about their uniformity
@@ -50,13 +52,22 @@ __device__ __forceinline__ void dma16(const u32x4& rs_in, uint32_t lds, uint32_t
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[1]),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[2]),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)rs_in[3])};
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds), "v"(voff), "s"(rs)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+        :
+        : "s"(lds), "v"(voff), "s"(rs)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(voff), "s"(rs)
+        : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -113,12 +124,13 @@ struct KcLoad {
       kel[i] = c * 8;
     }
   }
+  template <bool NT = false>
   __device__ __forceinline__ void issue(const u32x4& rs, uint32_t lds, int wave, int i, int kt,
                                         int K) const {
     const int q = i * NW + wave;
     const bool kin = kt * BK + kel[i] < K;
     const uint32_t v = (off[i] == kOOB || !kin) ? kOOB : off[i] + (uint32_t)kt * (BK * 2);
-    dma16(rs, lds + q * 1024, v);
+    dma16<NT>(rs, lds + q * 1024, v);
   }
 };
 
