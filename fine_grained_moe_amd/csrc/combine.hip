@@ -54,10 +54,11 @@ __global__ void __launch_bounds__(NT) combine_kernel(int T, int H, int K,
   const int nchunk = H / 8;
   for (int c = lane; c < nchunk; c += TPT) {
     u32x4 vr[KMAX], vs = u32x4{0u, 0u, 0u, 0u};
-    if (y_shared) vs = ((const u32x4*)(y_shared + (int64_t)t * H))[c];
+    // non-temporal loads: every row is read once here (alone 6 % faster)
+    if (y_shared) vs = __builtin_nontemporal_load((const u32x4*)(y_shared + (int64_t)t * H) + c);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (k < K) vr[k] = ((const u32x4*)(y_rows + (int64_t)rows[k] * H))[c];
+      if (k < K) vr[k] = __builtin_nontemporal_load((const u32x4*)(y_rows + (int64_t)rows[k] * H) + c);
     float acc[8], v[8];
     unpack8(vs, acc);
 #pragma unroll
@@ -157,8 +158,10 @@ __global__ void __launch_bounds__(NT) unpermute_add_kernel(int T, int H, int K,
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (k < K) vr[k] = ((const u32x4*)(dx_rows + (int64_t)rows[k] * H))[c];
-    if (dx_shared) vs = ((const u32x4*)(dx_shared + (int64_t)t * H))[c];
+      if (k < K) vr[k] = __builtin_nontemporal_load((const u32x4*)(dx_rows + (int64_t)rows[k] * H) + c);
+    // read once, as in the combine (the fused router backward + un-permute
+    // alone 10 % faster; the whole step 0.2 %)
+    if (dx_shared) vs = __builtin_nontemporal_load((const u32x4*)(dx_shared + (int64_t)t * H) + c);
     if (ROUTER) {
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
