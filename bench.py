@@ -46,12 +46,12 @@ STREAM_READ_GBS = 7050.0
 COUNTER_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_SOURCE_SHA256 = "7341e5ef1c3bf94b9fc07a151537583e70a8a6e4109d133897c7c703e29e1c04"
 TRAFFIC_KIB = {    # launch name -> (FETCH_SIZE KiB, WRITE_SIZE KiB), workload fwdbwd
-    "gate_up_fwd": (3072721.2, 405504.2), "down_fwd": (1087008.6, 491542.5),
-    "shared_gate_up_fwd": (348244.2, 135209.5), "shared_down_fwd": (180295.2, 81941.6),
-    "down_dgrad": (1879979.6, 270336.0), "gate_up_dgrad": (2554905.7, 491528.4),
-    "down_wgrad": (322414.0, 1802299.9), "gate_up_wgrad": (847144.8, 3605095.6),
-    "shared_down_dgrad": (352414.8, 90120.5), "shared_gate_up_dgrad": (360515.4, 81934.7),
-    "shared_down_wgrad": (217164.8, 28160.8), "shared_gate_up_wgrad": (434253.9, 56320.6),
+    "gate_up_fwd": (3075470.4, 405504.1), "down_fwd": (1103172.3, 491545.1),
+    "shared_gate_up_fwd": (348244.2, 135202.5), "shared_down_fwd": (180295.2, 81933.9),
+    "down_dgrad": (1895078.9, 270336.1), "gate_up_dgrad": (2605795.1, 491629.5),
+    "down_wgrad": (322732.3, 1802281.8), "gate_up_wgrad": (847809.1, 3605112.6),
+    "shared_down_dgrad": (352385.2, 90118.5), "shared_gate_up_dgrad": (360515.4, 81921.8),
+    "shared_down_wgrad": (217164.8, 28160.4), "shared_gate_up_wgrad": (434253.8, 56320.4),
 }
 
 
